@@ -1,0 +1,293 @@
+"""fp64 CPU oracle for the multi-token verify step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import or call this module; the library's
+product path never does.  It shares no code with the HIP path.
+
+What it computes, step by step, in the notation of the pages:
+
+* The verifier block.  A width-W block whose row 0 is the committed anchor
+  (the last committed token) and whose rows 1..W-1 are drafted tokens or mask
+  tokens.  "BitMTP: When Multi-Token Prediction Meets Low-Bit Large Language
+  Models", §3.3 (draft block d_1:D, accepted length a_i, one verifier-origin
+  token) and §3.4 M3 (width-(D+1) verifier block with the anchor);
+  "Efficient Training-Free Multi-Token Prediction via Embedding-Space
+  Probing", §2.D (block = last token + predicted tokens + mask tokens).
+
+* In-block visibility (``block_visibility``).
+  - CHAIN: the AR-causal verifier mask, row i sees rows 0..i (BitMTP §3.4 M3).
+  - TREE: a node sees itself and its ancestors (tree attention; BitMTP §2 on
+    Medusa's tree verification; Embedding-Space Probing §2.C-D, dynamic tree
+    with static tree masks).  The tree is a parent array with parent[i] < i.
+  - SEGMENT: Latent Causal Attention ("Dynamic Multi-Byte Prediction With
+    Hierarchical Language Models", Fig. 2 and §3): a position sees itself,
+    earlier positions of its own segment and the segments before it.  The
+    figure restricts the earlier segments to the immediately preceding one;
+    the workload statement lets a query see all earlier segments.  Both are
+    covered by ``seg_lookback`` (k >= 0 previous segments, or -1 = all).
+
+* Attention (``verify_attention``).  Every committed position 0..L-1 is
+  visible to every block row; block rows are visible per the mask above.
+  s = scale * q.k, p = softmax over the visible keys, out = sum p v,
+  lse = log sum exp s.  GQA: query head h uses KV head h // (Hq/Hkv).  The
+  committed cache is paged: logical token t lives in page
+  block_table[t // 16], slot t % 16.  Everything is done in fp64 over an
+  explicit dense [W, L+W] boolean mask.
+
+* Acceptance (``accept``).  The target token of row i is the argmax of its
+  logits (smallest id on ties).  Row 0 (the anchor) is always accepted
+  (Multi-Byte Prediction, Alg. 1: the next-byte head's output is always
+  accepted).  A drafted row i matches when its draft equals the target of its
+  parent (chain: row i-1), i.e. the verifier's prediction at the parent;
+  mask-token rows (draft < 0) never match.  The accepted path is the deepest
+  node whose whole root path matches (chain: the longest matching prefix,
+  BitMTP §3.3 speculative-only decoding; Multi-Byte Prediction §3.1 and §6.2,
+  left-to-right acceptance); ties go to the smaller node index.  The bonus
+  (verifier-origin) token is the target at the accepted node (BitMTP §3.3).
+
+* Commit (``kv_commit``).  The K/V rows of the accepted path, root first, are
+  copied to logical positions L, L+1, ..., L+a; rejected rows are never
+  written and the KV boundary advances by a+1 (BitMTP §3.4 M2: accepted draft
+  rows are promoted as consecutive rows; "BitNest: Bit-Nested Speculative
+  Decoding for Memory-Efficient LLM Inference Acceleration", §3.4 / §A.2:
+  retain accepted entries, discard the rejected suffix).  ``skip_root``
+  leaves the anchor's slot untouched, for callers whose anchor KV is already
+  in the cache (BitMTP §3.4 M2: promotion excludes the repeated anchor).
+
+Data errors (a parent index outside [0, i), segment ids that do not start at
+0 or step by other than 0/+1, an unknown mask kind, or an unmapped page for a
+slot the commit must write) are handled as the library's contract states:
+the sequence's attention output and log-sum-exp are NaN, its acceptance
+outputs are -1, and its commit is skipped (context length unchanged).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 16
+CHAIN, TREE, SEGMENT = 0, 1, 2
+
+
+# ----------------------------------------------------------------------------
+# in-block structure
+# ----------------------------------------------------------------------------
+
+def mask_is_valid(kind: int, ids: np.ndarray) -> bool:
+    """Whether a block's mask description is well formed."""
+    W = ids.shape[0]
+    if kind == CHAIN:
+        return True
+    if kind == TREE:
+        return all(0 <= int(ids[i]) < i for i in range(1, W))
+    if kind == SEGMENT:
+        if int(ids[0]) != 0:
+            return False
+        return all(int(ids[i]) - int(ids[i - 1]) in (0, 1) for i in range(1, W))
+    return False
+
+
+def acceptance_parents(kind: int, ids: np.ndarray) -> np.ndarray:
+    """Parent of every block row for acceptance: the tree's parent array, or
+    the previous row for a chain / segment block (left-to-right acceptance)."""
+    W = ids.shape[0]
+    if kind == TREE:
+        par = np.array(ids, dtype=np.int64)
+        par[0] = -1
+        return par
+    return np.arange(-1, W - 1, dtype=np.int64)
+
+
+def block_visibility(kind: int, ids: np.ndarray, seg_lookback: int) -> np.ndarray:
+    """[W, W] bool: vis[i, j] = block row i may attend to block row j."""
+    W = ids.shape[0]
+    vis = np.zeros((W, W), dtype=bool)
+    if kind == CHAIN:
+        for i in range(W):
+            for j in range(i + 1):
+                vis[i, j] = True
+    elif kind == TREE:
+        for i in range(W):
+            j = i
+            while j >= 0:
+                vis[i, j] = True
+                j = int(ids[j]) if j > 0 else -1
+    elif kind == SEGMENT:
+        for i in range(W):
+            si = int(ids[i])
+            for j in range(W):
+                sj = int(ids[j])
+                own = (sj == si) and (j <= i)
+                earlier = sj < si and (seg_lookback < 0 or si - sj <= seg_lookback)
+                vis[i, j] = own or earlier
+    else:
+        raise ValueError(f"unknown mask kind {kind}")
+    return vis
+
+
+def dense_mask(ctx_len: int, vis: np.ndarray) -> np.ndarray:
+    """[W, L+W] bool over (committed keys, block keys)."""
+    W = vis.shape[0]
+    m = np.zeros((W, ctx_len + W), dtype=bool)
+    m[:, :ctx_len] = True
+    m[:, ctx_len:] = vis
+    return m
+
+
+# ----------------------------------------------------------------------------
+# paged cache
+# ----------------------------------------------------------------------------
+
+def page_slot(block_row: np.ndarray, t: int) -> tuple[int, int]:
+    """Physical (page, slot) of logical token t of one sequence."""
+    return int(block_row[t // PAGE]), t % PAGE
+
+
+def gather_committed(cache: np.ndarray, block_row: np.ndarray, ctx_len: int) -> np.ndarray:
+    """Committed rows 0..L-1 of one sequence as a dense [L, Hkv, D] fp64 array."""
+    Hkv, D = cache.shape[2], cache.shape[3]
+    out = np.empty((ctx_len, Hkv, D), dtype=np.float64)
+    for t in range(ctx_len):
+        page, slot = page_slot(block_row, t)
+        out[t] = cache[page, slot]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+
+def attend(q: np.ndarray, keys: np.ndarray, values: np.ndarray, mask: np.ndarray,
+           scale: float):
+    """Masked softmax attention of W query rows over N keys, fp64.
+
+    q [W, D], keys/values [N, D], mask [W, N] -> out [W, D], lse [W], p [W, N]."""
+    s = scale * (q @ keys.T)
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    p = e / z
+    out = p @ values
+    lse = m[:, 0] + np.log(z[:, 0])
+    return out, lse, p
+
+
+def verify_attention(q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new,
+                     mask_kind, mask_ids, scale=None, seg_lookback=-1):
+    """Verify attention for a batch.
+
+    q [B,W,Hq,D]; k_cache/v_cache [pages,16,Hkv,D]; block_table [B,max_pages];
+    ctx_lens [B]; k_new/v_new [B,W,Hkv,D]; mask_kind [B]; mask_ids [B,W].
+    Returns out [B,W,Hq,D] and lse [B,W,Hq] in fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    B, W, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.full((B, W, Hq, D), np.nan)
+    lse = np.full((B, W, Hq), np.nan)
+    for b in range(B):
+        kind, ids = int(mask_kind[b]), np.asarray(mask_ids[b])
+        if not mask_is_valid(kind, ids):
+            continue
+        L = int(ctx_lens[b])
+        keys = np.concatenate([gather_committed(k_cache, block_table[b], L), k_new[b]], axis=0)
+        vals = np.concatenate([gather_committed(v_cache, block_table[b], L), v_new[b]], axis=0)
+        mask = dense_mask(L, block_visibility(kind, ids, seg_lookback))
+        for h in range(Hq):
+            kvh = h // g
+            o, l, _ = attend(q[b, :, h, :], keys[:, kvh, :], vals[:, kvh, :], mask, scale)
+            out[b, :, h, :] = o
+            lse[b, :, h] = l
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# acceptance
+# ----------------------------------------------------------------------------
+
+def target_ids(logits: np.ndarray) -> np.ndarray:
+    """Greedy verifier prediction per row: argmax, smallest id on ties."""
+    return np.argmax(np.asarray(logits), axis=-1).astype(np.int64)
+
+
+def accept(logits, draft_ids, mask_kind, mask_ids):
+    """Returns accept_len [B], accept_path [B,W] (-1 padded), bonus_id [B]."""
+    logits = np.asarray(logits)
+    B, W = logits.shape[0], logits.shape[1]
+    tgt = target_ids(logits)
+    acc_len = np.full(B, -1, dtype=np.int64)
+    path = np.full((B, W), -1, dtype=np.int64)
+    bonus = np.full(B, -1, dtype=np.int64)
+    for b in range(B):
+        kind, ids = int(mask_kind[b]), np.asarray(mask_ids[b])
+        if not mask_is_valid(kind, ids):
+            continue
+        par = acceptance_parents(kind, ids)
+        ok = np.zeros(W, dtype=bool)
+        depth = np.zeros(W, dtype=np.int64)
+        ok[0] = True
+        for i in range(1, W):
+            d = int(draft_ids[b, i])
+            p = int(par[i])
+            depth[i] = depth[p] + 1
+            ok[i] = ok[p] and d >= 0 and d == tgt[b, p]
+        best = 0
+        for i in range(1, W):
+            if ok[i] and depth[i] > depth[best]:
+                best = i
+        chain = []
+        j = best
+        while j >= 0:
+            chain.append(j)
+            j = int(par[j])
+        chain.reverse()
+        acc_len[b] = depth[best]
+        path[b, :len(chain)] = chain
+        bonus[b] = tgt[b, best]
+    return acc_len, path, bonus
+
+
+# ----------------------------------------------------------------------------
+# commit
+# ----------------------------------------------------------------------------
+
+def kv_commit(k_cache, v_cache, k_new, v_new, accept_len, accept_path, block_table,
+              ctx_lens, skip_root=False):
+    """Copies the accepted rows' K/V bytes into the cache pages.
+
+    Works on the raw element arrays (any dtype: the copy is exact).  Returns
+    (k_cache', v_cache', ctx_lens') as new arrays; the inputs are not
+    modified."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    ctx = np.array(ctx_lens, dtype=np.int64, copy=True)
+    B, W = accept_path.shape
+    num_pages = kc.shape[0]
+    for b in range(B):
+        a = int(accept_len[b])
+        if a < 0 or a > W - 1:
+            continue
+        L = int(ctx_lens[b])
+        first = 1 if skip_root else 0
+        writes = []
+        for k in range(first, a + 1):
+            t = L + k
+            row = int(accept_path[b, k])
+            if t // PAGE >= block_table.shape[1] or not (0 <= row < W):
+                writes = None
+                break
+            page, slot = page_slot(block_table[b], t)
+            if not (0 <= page < num_pages):
+                writes = None
+                break
+            writes.append((page, slot, row))
+        if writes is None:
+            continue
+        for page, slot, row in writes:
+            kc[page, slot] = k_new[b, row]
+            vc[page, slot] = v_new[b, row]
+        ctx[b] = L + a + 1
+    return kc, vc, ctx

@@ -1,0 +1,130 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case swaps one oracle helper for a copy carrying a plausible mistake (a
+dropped term, a wrong index, a transposed operand, an off-by-one) and checks
+that at least one pin from test_oracle_pins fails.  Everything runs on the
+CPU; the real oracle is restored after each case.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import verify_oracle as O
+from tests import test_oracle_pins as P
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _fails(fn, *args) -> bool:
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _tree_vis_without_self(kind, ids, lookback, _orig=O.block_visibility):
+    vis = _orig(kind, ids, lookback)
+    if kind == O.TREE:
+        np.fill_diagonal(vis[1:, 1:], False)
+    return vis
+
+
+def _segment_lookback_off_by_one(kind, ids, lookback, _orig=O.block_visibility):
+    if kind == O.SEGMENT and lookback > 0:
+        return _orig(kind, ids, lookback - 1)
+    return _orig(kind, ids, lookback)
+
+
+def _gather_shifted(cache, block_row, ctx_len):
+    out = np.empty((ctx_len,) + cache.shape[2:], dtype=np.float64)
+    for t in range(ctx_len):
+        tt = min(t + 1, ctx_len - 1)
+        out[t] = cache[int(block_row[tt // O.PAGE]), tt % O.PAGE]
+    return out
+
+
+def _gather_slot_major(cache, block_row, ctx_len):
+    out = np.empty((ctx_len,) + cache.shape[2:], dtype=np.float64)
+    for t in range(ctx_len):
+        out[t] = cache[int(block_row[t % O.PAGE]) if t % O.PAGE < len(block_row) else 0, t // O.PAGE]
+    return out
+
+
+def _attend_no_scale(q, keys, values, mask, scale, _orig=O.attend):
+    return _orig(q, keys, values, mask, 1.0)
+
+
+def _attend_values_are_keys(q, keys, values, mask, scale, _orig=O.attend):
+    return _orig(q, keys, keys, mask, scale)
+
+
+def _attend_lse_without_max(q, keys, values, mask, scale, _orig=O.attend):
+    out, lse, p = _orig(q, keys, values, mask, scale)
+    s = np.where(mask, scale * (q @ keys.T), -np.inf)
+    return out, lse - s.max(axis=1), p
+
+
+def _parents_self(kind, ids, _orig=O.acceptance_parents):
+    par = _orig(kind, ids)
+    if kind != O.TREE:
+        par = np.arange(len(ids)) - 0  # compares row i with its own prediction
+        par[0] = -1
+    return par
+
+
+def _targets_argmin(logits):
+    return np.argmin(np.asarray(logits), axis=-1)
+
+
+def _targets_last_on_ties(logits):
+    lg = np.asarray(logits)
+    V = lg.shape[-1]
+    return (V - 1 - np.argmax(lg[..., ::-1], axis=-1)).astype(np.int64)
+
+
+def _page_slot_swapped(block_row, t):
+    return int(block_row[t // O.PAGE]), (t + 1) % O.PAGE
+
+
+MUTANTS = [
+    ("block_visibility", _tree_vis_without_self, [(P.test_tree_visibility_is_ancestor_closure, 3),
+                                                  (P.test_tree_golden_fixture,)]),
+    ("block_visibility", _segment_lookback_off_by_one, [(P.test_lca_golden_fixture,)]),
+    ("gather_committed", _gather_shifted, [(P.test_attention_matches_library_sdpa, "chain", -1, 0)]),
+    ("gather_committed", _gather_slot_major, [(P.test_attention_matches_library_sdpa, "tree", -1, 1)]),
+    ("attend", _attend_no_scale, [(P.test_attention_matches_library_sdpa, "tree", -1, 0)]),
+    ("attend", _attend_values_are_keys, [(P.test_single_row_block_is_plain_decode_attention, 8, 2)]),
+    ("attend", _attend_lse_without_max, [(P.test_equal_keys_average_the_visible_values, "chain")]),
+    ("acceptance_parents", _parents_self, [(P.test_full_match_accepts_the_whole_chain,)]),
+    ("target_ids", _targets_argmin, [(P.test_accept_golden_tree,)]),
+    ("target_ids", _targets_last_on_ties, [(P.test_argmax_ties_take_the_smallest_id,)]),
+    ("page_slot", _page_slot_swapped, [(P.test_commit_writes_exactly_the_accepted_rows, False)]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", MUTANTS,
+                         ids=[f"{n}:{m.__name__}" for n, m, _ in MUTANTS])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setattr(O, name, mutant)
+    for pin in pins:
+        assert _fails(pin[0], *pin[1:]), f"{pin[0].__name__} did not catch {mutant.__name__}"
+
+
+def test_gqa_head_mapping_mistake_is_caught(monkeypatch):
+    """Query head h reading KV head h % Hkv instead of h // group."""
+    real = O.verify_attention
+
+    def mutated(q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new, mask_kind,
+                mask_ids, scale=None, seg_lookback=-1):
+        Hq, Hkv = q.shape[2], k_cache.shape[2]
+        g = Hq // Hkv
+        perm = np.array([(h % Hkv) * g + h // Hkv for h in range(Hq)])
+        inv = np.argsort(perm)  # slot perm[h] of the real call carries head h
+        out, lse = real(np.asarray(q)[:, :, inv], k_cache, v_cache, block_table, ctx_lens,
+                        k_new, v_new, mask_kind, mask_ids, scale, seg_lookback)
+        return out[:, :, perm], lse[:, :, perm]
+
+    monkeypatch.setattr(O, "verify_attention", mutated)
+    assert _fails(P.test_attention_matches_library_sdpa, "mixed", -1, 0)
