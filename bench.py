@@ -1,0 +1,247 @@
+"""Verify-step benchmark on one MI355X.
+
+One step = the whole verify hot path over one batch of synthetic input:
+split-K verify attention (partial + combine kernels), greedy acceptance and
+KV commit (one fused launch).  Inputs are resident in HBM before timing.
+Cold-cache by default: the KV page pool is replicated R times (R * KV >= 1 GB,
+well above the 256 MB Infinity Cache) and step i reads replica i % R.
+
+Prints ONE JSON line.  `value` is committed-KV GB/s of the whole step;
+`roofline` is the split-K partial kernel's algorithmic bytes per launch over
+its mean duration from HIP events recorded around each launch in the timed
+region; `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from speculative_decoding_verify_mtp_amd import inputs as I  # noqa: E402
+from speculative_decoding_verify_mtp_amd import lib  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "bitnet2b_chain"
+KERNEL_SOURCES = ["attn_mfma.hpp", "attn_valu.hpp", "common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "speculative_decoding_verify_mtp_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def elem_bytes(wl: I.Workload) -> int:
+    return 4 if wl.dtype == "f32" else 2
+
+
+def algorithmic_bytes(wl: I.Workload, ctx: np.ndarray) -> dict:
+    """Bytes the method must move per step (not what the kernels happen to move)."""
+    e = elem_bytes(wl)
+    B, W, Hq, Hkv, D = wl.B, wl.W, wl.Hq, wl.Hkv, wl.D
+    kv = int(np.sum(ctx.astype(np.int64))) * Hkv * D * 2 * e
+    q = B * W * Hq * D * e
+    new_kv = B * W * Hkv * D * 2 * e
+    out = B * W * Hq * D * 4 + B * W * Hq * 4
+    table = int(np.sum((ctx.astype(np.int64) + 15) // 16)) * 4
+    logits = B * W * wl.vocab * 4
+    return dict(kv=kv, partial=kv + q + new_kv + table, step=kv + q + new_kv + out + table + logits)
+
+
+def traffic_from_profile(workload: str, launch_bytes: int) -> float | None:
+    """HBM bytes per partial launch from the committed rocprofv3 counter summary,
+    scaled by the copy-kernel calibration, if it was taken on the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+def cpu_baseline(wl: I.Workload, seed: int, budget_s: float) -> dict:
+    """fp64 oracle on a bounded sample: whole steps (attention + acceptance +
+    commit) of the same workload on the host, repeated for about budget_s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import verify_oracle as O
+
+    sample = wl
+    # bounded sample: at most 4 sequences of the batch
+    if wl.B > 4:
+        sample = wl.scaled(B=4)
+    inp = I.make_inputs(sample, seed, device="cpu")
+    host = inp["host"]
+    f64 = lambda t: t.double().numpy()
+    q, kc, vc = f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"])
+    kn, vn = f64(inp["k_new"]), f64(inp["v_new"])
+    logits = inp["logits"].numpy()
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        O.verify_attention(q, kc, vc, host["block_table"], host["ctx_lens"], kn, vn,
+                           host["mask_kind"], host["mask_ids"], inp["scale"], wl.seg_lookback)
+        n, path, _ = O.accept(logits, host["draft_ids"], host["mask_kind"], host["mask_ids"])
+        O.kv_commit(kc, vc, kn, vn, n, path, host["block_table"], host["ctx_lens"])
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    kv = algorithmic_bytes(sample, host["ctx_lens"])["kv"]
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": kv * steps / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} whole oracle steps of {sample.B} sequence(s) of {wl.name} "
+                      f"(ctx {host['ctx_lens'].tolist()}) in {dt:.1f} s, fp64 numpy"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(I.WORKLOADS))
+    ap.add_argument("--seg-lookback", type=int, default=None)
+    ap.add_argument("--replicas", type=int, default=0, help="KV pool replicas (0 = auto, >= 1 GB)")
+    ap.add_argument("--warm", action="store_true", help="one replica (cache-warm numbers)")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the verify step is measured on one "
+              "GPU's share); --gpus must be 1", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = I.WORKLOADS[args.workload]
+    if args.seg_lookback is not None:
+        wl = wl.scaled(seg_lookback=args.seg_lookback)
+    seed = I.workload_seed(args.workload)
+    inp = I.make_inputs(wl, seed, device=dev)
+    host = inp["host"]
+    ctx = host["ctx_lens"]
+    nbytes = algorithmic_bytes(wl, ctx)
+    pool = inp["k_cache"].shape[0]
+
+    # cold-cache replicas of the page pool
+    if args.warm:
+        R = 1
+    elif args.replicas > 0:
+        R = args.replicas
+    else:
+        R = max(1, math.ceil(1.0e9 / max(nbytes["kv"], 1)))
+    R = min(R, max(1, (2**31 - 1) // pool))
+    k_all = inp["k_cache"].repeat(R, 1, 1, 1)
+    v_all = inp["v_cache"].repeat(R, 1, 1, 1)
+    bt = inp["block_table"]
+    tables = [torch.where(bt >= 0, bt + r * pool, bt).contiguous() for r in range(R)]
+    del inp["k_cache"], inp["v_cache"]
+
+    max_ctx = int(ctx.max())
+    shape = lib.shape_of(inp["q"], k_all, bt, max_ctx_len=max_ctx, scale=inp["scale"],
+                         seg_lookback=wl.seg_lookback, split_tokens=args.split_tokens)
+    workspace = torch.empty(max(lib.workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
+    B, W, Hq, D = inp["q"].shape
+    out = torch.empty((B, W, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, W, Hq), dtype=torch.float32, device=dev)
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+    apath = torch.empty((B, W), dtype=torch.int32, device=dev)
+    bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    ctx_out = torch.empty_like(inp["ctx_lens"])
+
+    def step(r: int, ev=None):
+        common = (inp["q"], k_all, v_all, tables[r], inp["ctx_lens"], inp["k_new"], inp["v_new"],
+                  inp["mask_kind"], inp["mask_ids"])
+        if ev is not None:
+            ev[0].record()
+        lib.verify_attn(*common, out=out, lse=lse, workspace=workspace, shape=shape,
+                        phase="partial")
+        if ev is not None:
+            ev[1].record()
+        lib.verify_attn(*common, out=out, lse=lse, workspace=workspace, shape=shape,
+                        phase="combine")
+        lib.accept_commit(inp["logits"], inp["draft_ids"], inp["mask_kind"], inp["mask_ids"],
+                          inp["k_new"], inp["v_new"], tables[r], inp["ctx_lens"], k_all, v_all,
+                          accept_len=alen, accept_path=apath, bonus_id=bonus,
+                          ctx_lens_out=ctx_out)
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i % R, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if lib.device_status(clear=True) != 0:
+        print("bench.py: the device reported a data error", file=sys.stderr)
+        return 3
+
+    sec_per_step = (t1 - t0) / K
+    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    achieved = nbytes["partial"] / (partial_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(wl.name, nbytes["partial"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, seed, args.cpu_seconds)
+
+    mask_desc = {"chain": "chain", "tree": "tree", "segment": f"segment(lookback={wl.seg_lookback})",
+                 "mixed": "half chain, half tree"}[wl.masks]
+    rec = {
+        "metric": "verify-step KV GB/s and W-token blocks/sec at 1 GPU; % of HBM roofline",
+        "value": round(nbytes["kv"] / sec_per_step / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) K/V/Q, paged KV, shuffled pages)",
+        "config": {"workload": wl.name, "B": wl.B, "W": wl.W, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "D": wl.D, "ctx": [int(ctx.min()), int(ctx.max())], "mask": mask_desc,
+                   "page_size": 16, "kv_replicas": R, "cache": "warm" if R == 1 else "cold",
+                   "split_tokens": args.split_tokens or "auto"},
+        "blocks_per_s": round(wl.B / sec_per_step, 1),
+        "kv_bytes_per_step": nbytes["kv"],
+        "hbm_frac_step": round(nbytes["kv"] / sec_per_step / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "attn_partial (split-K verify attention)",
+                     "kernel_us": round(partial_ms * 1e3, 3),
+                     "algorithmic_bytes": nbytes["partial"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

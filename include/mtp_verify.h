@@ -1,0 +1,219 @@
+/*
+ * mtp_verify.h -- C ABI of the multi-token verify step on MI355X (gfx950).
+ *
+ * The verify step of multi-token / speculative decoding, as the pages state
+ * the problem:
+ *
+ *   1. verify attention: a width-W block (row 0 = the committed anchor, rows
+ *      1..W-1 = drafted or mask tokens) attends over the sequence's committed
+ *      paged KV cache plus the block's own K/V under an in-block mask
+ *      ("BitMTP: When Multi-Token Prediction Meets Low-Bit Large Language
+ *      Models", Sec. 3.3 and Sec. 3.4 M3: width-(D+1) verifier block with the
+ *      anchor and an AR-causal mask; "Efficient Training-Free Multi-Token
+ *      Prediction via Embedding-Space Probing", Sec. 2 Methodology: block =
+ *      last token + predicted tokens + mask tokens, tree verification with
+ *      static tree masks; "Dynamic Multi-Byte Prediction With Hierarchical
+ *      Language Models", Fig. 2 and Sec. 3: the Latent Causal Attention mask);
+ *   2. acceptance: the greedy verifier's argmax at every block row decides
+ *      the accepted prefix (chain) or root path (tree) and one
+ *      verifier-origin ("bonus") token (BitMTP Sec. 3.3, speculative-only
+ *      decoding; Multi-Byte Prediction Sec. 3.1 and Sec. 6.2);
+ *   3. KV commit: only the accepted rows' K/V are written into the cache, as
+ *      consecutive rows after the committed boundary, and the boundary
+ *      advances (BitMTP Sec. 3.4 M2; "BitNest: Bit-Nested Speculative
+ *      Decoding for Memory-Efficient LLM Inference Acceleration", Sec. 3.4:
+ *      keep accepted entries, discard the rejected suffix).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers owned by the caller, row-major
+ *   and densely packed in the layouts given below.  The library allocates
+ *   no device memory; verify attention takes a caller-provided workspace.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream) and returns once the kernels are enqueued.  The functions are
+ *   stateless and reentrant; calls that write the same buffers must be
+ *   ordered by the caller (same stream or events).
+ * - Host-checkable argument errors return a non-zero mtp_status and enqueue
+ *   nothing.  Data errors found on the device (bad mask ids, a context length
+ *   out of range, an unmapped page) never fault: they poison the affected
+ *   outputs as documented per call and OR a bit into a per-device sticky
+ *   status word read by mtp_get_device_status().
+ * - Context length ctx_lens[b] counts the committed tokens strictly before
+ *   block row 0.  Logical token t of sequence b lives in page
+ *   block_table[b][t / 16], slot t % 16.
+ * - Mask description per sequence: mask_kind[b] (uint8) and mask_ids[b][W]
+ *   (int32):
+ *     MTP_MASK_CHAIN   : ids ignored; row i sees block rows 0..i.
+ *     MTP_MASK_TREE    : ids = parent array, ids[0] ignored (root), and
+ *                        0 <= ids[i] < i for i >= 1; row i sees itself and
+ *                        its ancestors.
+ *     MTP_MASK_SEGMENT : ids = segment ids, ids[0] == 0, each step 0 or +1;
+ *                        row i sees earlier rows of its own segment, itself,
+ *                        and the seg_lookback previous segments (-1 = all
+ *                        earlier segments; 1 = the LCA mask of Fig. 2).
+ *   Every committed token is visible to every block row.
+ */
+#ifndef MTP_VERIFY_H
+#define MTP_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTP_ABI_VERSION 1
+#define MTP_PAGE_SIZE 16
+#define MTP_MAX_W 64
+
+typedef enum {
+  MTP_OK = 0,
+  MTP_ERR_NULL = 1,        /* a required pointer is NULL */
+  MTP_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  MTP_ERR_UNSUPPORTED = 3, /* valid but not implemented (D, dtype, page size) */
+  MTP_ERR_WORKSPACE = 4,   /* workspace too small */
+  MTP_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+} mtp_status;
+
+typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
+
+typedef enum { MTP_MASK_CHAIN = 0, MTP_MASK_TREE = 1, MTP_MASK_SEGMENT = 2 } mtp_mask_kind;
+
+/* Bits of the device status word. */
+#define MTP_DEV_BAD_MASK 0x1u   /* mask_kind unknown or mask_ids malformed */
+#define MTP_DEV_BAD_CTX 0x2u    /* ctx_lens[b] < 0 or > max_ctx_len */
+#define MTP_DEV_BAD_PAGE 0x4u   /* block_table entry outside [0, num_pages) where read or written */
+#define MTP_DEV_BAD_ACCEPT 0x8u /* commit given accept_len / accept_path out of range */
+
+/* Sizes of one verify step. */
+typedef struct mtp_shape {
+  int32_t B;                 /* sequences in the batch, >= 0 (0 = no-op) */
+  int32_t W;                 /* block width, 1..64 (row 0 = anchor) */
+  int32_t Hq;                /* query heads; Hq % Hkv == 0, group g = Hq / Hkv */
+  int32_t Hkv;               /* KV heads, >= 1 */
+  int32_t D;                 /* head dim: 64 or 128 */
+  int32_t page_size;         /* tokens per page: must be 16 */
+  int32_t num_pages;         /* pages in each of k_cache / v_cache */
+  int32_t max_pages_per_seq; /* columns of block_table */
+  int32_t max_ctx_len;       /* upper bound of every ctx_lens[b]; <= 16 * max_pages_per_seq */
+  int32_t dtype;             /* mtp_dtype of q, k_cache, v_cache, k_new, v_new */
+  float scale;               /* softmax scale; 0 selects 1/sqrt(D) */
+  int32_t seg_lookback;      /* SEGMENT masks: -1 = all earlier segments, k >= 0 = k previous */
+  int32_t split_tokens;      /* committed tokens per split-K work item; 0 = automatic,
+                                else a positive multiple of 32 */
+} mtp_shape;
+
+/* Returns MTP_ABI_VERSION. */
+int32_t mtp_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* mtp_status_string(int32_t status);
+
+/* Bytes of device workspace mtp_verify_attn needs for `shape` (split-K
+ * partials: per sequence, split, KV head and block-row x group-member row,
+ * D accumulators plus running max and sum, fp32).  Depends on B, W, Hq, Hkv,
+ * D, dtype, max_ctx_len and split_tokens only. */
+mtp_status mtp_verify_attn_workspace_size(const mtp_shape* shape, size_t* bytes);
+
+/* Verify attention (the step's attention over committed + in-block keys).
+ *
+ *   q            [B, W, Hq, D]           dtype
+ *   k_cache      [num_pages, 16, Hkv, D] dtype (read only)
+ *   v_cache      [num_pages, 16, Hkv, D] dtype (read only)
+ *   block_table  [B, max_pages_per_seq]  int32
+ *   ctx_lens     [B]                     int32
+ *   k_new, v_new [B, W, Hkv, D]          dtype (the block's own K/V)
+ *   mask_kind    [B] uint8, mask_ids [B, W] int32 (see above)
+ *   out          [B, W, Hq, D]           fp32  (written)
+ *   lse          [B, W, Hq]              fp32 natural-log sum-exp of the
+ *                                        scaled scores, or NULL
+ *   workspace    >= mtp_verify_attn_workspace_size bytes, 16-byte aligned
+ *
+ * Query head h reads KV head h / (Hq / Hkv).  out[b,i,h] =
+ * sum_t softmax_t(scale * q.k_t) v_t over the visible keys.  Data errors:
+ * a sequence with a malformed mask or a context length outside
+ * [0, max_ctx_len] gets NaN in all of its out / lse rows; a block-table
+ * entry outside [0, num_pages) inside the committed range makes the rows
+ * that read it NaN.  Both set the corresponding status bit. */
+mtp_status mtp_verify_attn(const mtp_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* ctx_lens, const void* k_new, const void* v_new,
+                           const uint8_t* mask_kind, const int32_t* mask_ids, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two launches mtp_verify_attn makes, for callers that time or order
+ * them separately: the split-K partial kernel (writes only the workspace)
+ * and the combine kernel (reads the workspace, writes out / lse).  Same
+ * arguments and checks as mtp_verify_attn; partial must precede combine on
+ * the same workspace. */
+mtp_status mtp_verify_attn_partial(const mtp_shape* shape, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* ctx_lens, const void* k_new,
+                                   const void* v_new, const uint8_t* mask_kind,
+                                   const int32_t* mask_ids, float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+mtp_status mtp_verify_attn_combine(const mtp_shape* shape, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* ctx_lens, const void* k_new,
+                                   const void* v_new, const uint8_t* mask_kind,
+                                   const int32_t* mask_ids, float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Greedy acceptance (uses B and W of `shape` only).
+ *
+ *   logits      [B, W, V] fp32: the verifier's logits at each block row
+ *   draft_ids   [B, W] int32: drafted token of each row (row 0 ignored;
+ *               < 0 marks a mask token, which is never accepted)
+ *   accept_len  [B] int32 (written): accepted drafts, 0..W-1
+ *   accept_path [B, W] int32 (written): block rows of the accepted path,
+ *               root first, padded with -1
+ *   bonus_id    [B] int32 (written): the verifier-origin token
+ *
+ * target[i] = argmax_v logits[b,i,v] (smallest id on ties).  Row i >= 1
+ * matches when draft_ids[b,i] >= 0 and equals target[parent(i)], where
+ * parent(i) is the tree parent (TREE) or i-1 (CHAIN, SEGMENT).  The accepted
+ * node is the deepest node whose whole root path matches (smallest index
+ * on ties); the root is always accepted; bonus = target[accepted node].
+ * A malformed mask writes -1 to all three outputs of that sequence.
+ * Logits must be finite (NaN handling is unspecified). */
+mtp_status mtp_accept(const mtp_shape* shape, const float* logits, int32_t V,
+                      const int32_t* draft_ids, const uint8_t* mask_kind,
+                      const int32_t* mask_ids, int32_t* accept_len, int32_t* accept_path,
+                      int32_t* bonus_id, void* stream);
+
+/* KV commit.  For path position k = (skip_root ? 1 : 0) .. accept_len[b],
+ * copies the bytes of k_new/v_new[b, accept_path[b][k], :, :] to logical
+ * position ctx_lens_in[b] + k of k_cache/v_cache, then writes
+ * ctx_lens_out[b] = ctx_lens_in[b] + accept_len[b] + 1 (may alias
+ * ctx_lens_in).  skip_root = 1 leaves the anchor's slot untouched (callers
+ * whose anchor K/V is already cached).  The caller maps every page the
+ * commit writes.  A sequence whose accept_len is outside [0, W-1], whose
+ * path holds a row outside [0, W), whose context length is negative or
+ * whose target slots are unmapped is not written at all and keeps its
+ * context length (status bit set). */
+mtp_status mtp_kv_commit(const mtp_shape* shape, const void* k_new, const void* v_new,
+                         const int32_t* accept_len, const int32_t* accept_path,
+                         const int32_t* block_table, const int32_t* ctx_lens_in,
+                         int32_t* ctx_lens_out, int32_t skip_root, void* k_cache,
+                         void* v_cache, void* stream);
+
+/* mtp_accept followed by mtp_kv_commit in one launch (one workgroup per
+ * sequence); same arguments, same results. */
+mtp_status mtp_accept_commit(const mtp_shape* shape, const float* logits, int32_t V,
+                             const int32_t* draft_ids, const uint8_t* mask_kind,
+                             const int32_t* mask_ids, int32_t* accept_len,
+                             int32_t* accept_path, int32_t* bonus_id, const void* k_new,
+                             const void* v_new, const int32_t* block_table,
+                             const int32_t* ctx_lens_in, int32_t* ctx_lens_out,
+                             int32_t skip_root, void* k_cache, void* v_cache, void* stream);
+
+/* Reads (and with clear != 0 resets) the current device's sticky status word
+ * into *bits.  Synchronous: waits for all work on the device. */
+mtp_status mtp_get_device_status(uint32_t* bits, int32_t clear);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTP_VERIFY_H */

@@ -1,0 +1,211 @@
+// Greedy acceptance and KV commit.  One workgroup (4 waves) per sequence.
+//
+// Acceptance: the four waves take the block rows in turn and reduce the argmax
+// of each row's logits (smallest id on ties).  Wave 0 then maps block node i
+// to lane i: match_i = (draft_i >= 0 and draft_i == target[parent_i]); the
+// node is accepted when every node on its root path matches, i.e. when its
+// ancestor-or-self bit row has no non-matching node; the accepted node is the
+// deepest such node (smallest index on ties), found by one wave max over
+// depth * 64 + (63 - i).  The root path is the bit row of that node, so lane
+// i writes itself to path position popcount(bits below i).
+//
+// Commit: lanes of wave 0 validate one path position each (row index, page
+// mapping); then all 256 threads copy the accepted rows in 16-byte chunks.  A
+// K/V row of one token is Hkv * D contiguous elements both in k_new and in a
+// cache slot, so each accepted position is one contiguous copy.
+#pragma once
+
+#include "common.hpp"
+
+namespace mtpv {
+
+struct AcceptParams {
+  const float* logits;  // [B, W, V]
+  const int32_t* draft_ids;
+  const uint8_t* mask_kind;
+  const int32_t* mask_ids;
+  int32_t* accept_len;
+  int32_t* accept_path;
+  int32_t* bonus_id;
+  int B, W, V;
+};
+
+struct CommitParams {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* accept_len;   // read when the acceptance is not fused
+  const int32_t* accept_path;  // read when the acceptance is not fused
+  const int32_t* block_table;
+  const int32_t* ctx_in;
+  int32_t* ctx_out;
+  void* k_cache;
+  void* v_cache;
+  int skip_root;
+  int W, max_pages, num_pages;
+  int row_bytes;  // Hkv * D * element size, a multiple of 16
+};
+
+// Argmax of every block row into s_tgt[0..W).  All 256 threads take part.
+__device__ inline void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  for (int i = wv; i < p.W; i += 4) {
+    const float* row = p.logits + ((size_t)b * p.W + i) * p.V;
+    float bv = neg_inf();
+    int bi = 0x7fffffff;
+    for (int v = lane; v < p.V; v += kWave) {
+      const float x = row[v];
+      if (x > bv || bi == 0x7fffffff) {
+        bv = x;
+        bi = v;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) s_tgt[i] = bi;
+  }
+}
+
+// Acceptance of sequence b by wave 0 (lane = node).  Returns the accepted
+// length (-1 for a malformed mask) and fills s_path[0..len] with the path.
+__device__ inline int wave_accept(const AcceptParams& p, int b, const int* s_tgt, int* s_path) {
+  const int lane = threadIdx.x & 63;
+  const int W = p.W;
+  const bool in = lane < W;
+  const int kind = p.mask_kind[b];
+  const int32_t* ids = p.mask_ids + (size_t)b * W;
+  bool ok;
+  uint64_t anc;
+  int par;
+  if (kind == MTP_MASK_TREE) {
+    anc = node_visibility(kind, ids, W, -1, lane, ok);
+    par = (in && lane >= 1 && ok) ? ids[lane] : 0;
+  } else {
+    node_visibility(kind, ids, W, -1, lane, ok);  // validates the description
+    anc = in ? (~0ull >> (63 - lane)) : 0ull;
+    par = lane >= 1 ? lane - 1 : 0;
+  }
+  int32_t* path = p.accept_path + (size_t)b * W;
+  if (!ok) {
+    if (in) path[lane] = -1;
+    if (lane == 0) {
+      p.accept_len[b] = -1;
+      p.bonus_id[b] = -1;
+      raise_status(MTP_DEV_BAD_MASK);
+    }
+    return -1;
+  }
+  const int d = in ? p.draft_ids[(size_t)b * W + lane] : -1;
+  const bool match = in && lane >= 1 && d >= 0 && d == s_tgt[par];
+  const uint64_t mm = __ballot(match) | 1ull;
+  const bool acc = in && (anc & ~mm) == 0ull;
+  const int depth = __popcll(anc) - 1;
+  const int key = wave_max_int(acc ? depth * 64 + (63 - lane) : -1);
+  const int best = 63 - (key & 63);
+  const int len = key >> 6;
+  const uint64_t ab = shfl64(anc, best);
+  if (in) {
+    if ((ab >> lane) & 1ull) {
+      const int pos = __popcll(ab & ((1ull << lane) - 1ull));
+      path[pos] = lane;
+      s_path[pos] = lane;
+    } else if (lane > len) {
+      path[lane] = -1;
+    }
+  }
+  if (lane == 0) {
+    p.accept_len[b] = len;
+    p.bonus_id[b] = s_tgt[best];
+  }
+  return len;
+}
+
+// Commit of sequence b.  `a` (accepted length) and s_path are valid in wave 0
+// when fused; otherwise pass fused = false and they are read from memory.
+template <bool kFused>
+__device__ inline void block_commit(const CommitParams& p, int b, int a_fused, const int* s_path,
+                                    int* s_src, int* s_dst, int* s_meta) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < kWave) {
+    const int a = kFused ? a_fused : p.accept_len[b];
+    const int L = p.ctx_in[b];
+    const int first = p.skip_root ? 1 : 0;
+    const bool a_ok = a >= 0 && a <= p.W - 1 && L >= 0;
+    bool bad_k = false;
+    if (a_ok && lane >= first && lane <= a) {
+      const int row = kFused ? s_path[lane] : p.accept_path[(size_t)b * p.W + lane];
+      const int t = L + lane;
+      const int pi = t >> 4;
+      const int pg = pi < p.max_pages ? p.block_table[(size_t)b * p.max_pages + pi] : -1;
+      bad_k = row < 0 || row >= p.W || pg < 0 || pg >= p.num_pages;
+      s_src[lane] = row;
+      s_dst[lane] = pg * kPage + (t & 15);
+    }
+    const bool bad = __ballot(bad_k) != 0ull;
+    if (lane == 0) {
+      const bool good = a_ok && !bad;
+      s_meta[0] = good ? a : -1;
+      s_meta[1] = first;
+      p.ctx_out[b] = good ? L + a + 1 : L;  // L was read above by this lane
+      if (!good) raise_status(a_ok ? MTP_DEV_BAD_PAGE : MTP_DEV_BAD_ACCEPT);
+    }
+  }
+  __syncthreads();
+  const int a = s_meta[0];
+  const int first = s_meta[1];
+  if (a < first) return;
+  const int chunks = p.row_bytes >> 4;
+  const int total = (a - first + 1) * chunks;
+  const char* kn = static_cast<const char*>(p.k_new);
+  const char* vn = static_cast<const char*>(p.v_new);
+  char* kc = static_cast<char*>(p.k_cache);
+  char* vc = static_cast<char*>(p.v_cache);
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int k = first + idx / chunks;
+    const size_t ch = (size_t)(idx % chunks) * 16;
+    const size_t src = ((size_t)b * p.W + s_src[k]) * p.row_bytes + ch;
+    const size_t dst = (size_t)s_dst[k] * p.row_bytes + ch;
+    *reinterpret_cast<uint4*>(kc + dst) = *reinterpret_cast<const uint4*>(kn + src);
+    *reinterpret_cast<uint4*>(vc + dst) = *reinterpret_cast<const uint4*>(vn + src);
+  }
+}
+
+__global__ __launch_bounds__(256) void accept_kernel(AcceptParams p) {
+  __shared__ int s_tgt[MTP_MAX_W];
+  __shared__ int s_path[MTP_MAX_W];
+  const int b = blockIdx.x;
+  block_argmax(p, b, s_tgt);
+  __syncthreads();
+  if (threadIdx.x < kWave) wave_accept(p, b, s_tgt, s_path);
+}
+
+__global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
+  __shared__ int s_src[MTP_MAX_W];
+  __shared__ int s_dst[MTP_MAX_W];
+  __shared__ int s_meta[2];
+  block_commit<false>(p, blockIdx.x, 0, nullptr, s_src, s_dst, s_meta);
+}
+
+__global__ __launch_bounds__(256) void accept_commit_kernel(AcceptParams ap, CommitParams cp) {
+  __shared__ int s_tgt[MTP_MAX_W];
+  __shared__ int s_path[MTP_MAX_W];
+  __shared__ int s_src[MTP_MAX_W];
+  __shared__ int s_dst[MTP_MAX_W];
+  __shared__ int s_meta[2];
+  const int b = blockIdx.x;
+  block_argmax(ap, b, s_tgt);
+  __syncthreads();
+  int a = -1;
+  if (threadIdx.x < kWave) a = wave_accept(ap, b, s_tgt, s_path);
+  __syncthreads();
+  block_commit<true>(cp, b, a, s_path, s_src, s_dst, s_meta);
+}
+
+}  // namespace mtpv

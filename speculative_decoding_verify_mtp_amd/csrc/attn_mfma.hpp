@@ -1,0 +1,342 @@
+// Split-K verify attention on bf16 MFMA (gfx950 v_mfma_f32_16x16x32_bf16).
+//
+// One wave = one work item: (sequence b, KV head, row block, split of the
+// committed context).  The rows of a KV head are the W block rows times the
+// g query heads of its GQA group (row rho = w * g + j reads query head
+// kvh * g + j); a row block is RB tiles of 16 rows.  Every K/V row a wave
+// loads feeds all RB*16 rows, so each committed byte is read once per row
+// block.
+//
+// Scores are computed transposed, S^T = K Q^T, so that the probabilities come
+// out of the accumulator already in the operand layout the PV product needs,
+// and PV is computed as acc^T = V^T P^T:
+//   * K is MFMA operand A: lane (i = lane%16, q = lane/16) holds key i,
+//     elements [32m + 8q, +8) for d-chunk m -- for each chunk the four lanes
+//     of a key read 64 contiguous bytes.
+//   * Q^T is operand B with the same d mapping, loaded once per item.
+//   * S^T accumulator: lane (j, q) holds S[row j][keys 4q..4q+3] of a 16-key
+//     tile, so a lane owns one row and the row reductions need only the two
+//     cross-quarter shuffles.
+//   * V^T is operand A of PV.  The output d-index of MFMA column tile t, row
+//     i is d = (D/16) * i + t, so lane (i, q) needs V[key][(D/16) i .. +D/16)
+//     for its 8 keys: sixteen lanes read one whole K/V row per load (fully
+//     coalesced), and operand t takes element t of each of the 8 vectors.
+//   * P^T is operand B of PV: lane (j, q) supplies row j, keys
+//     {4q..4q+3} of tile 0 and of tile 1 -- exactly the S^T registers.
+//   * acc^T accumulator: lane (j, q) ends up owning row j, d in
+//     [q * D/4, (q+1) * D/4).
+// K and V go straight from HBM to registers with 16-byte (D=128) or 8-byte
+// (D=64) loads; no LDS is needed.  Online softmax runs in the log2 domain.
+#pragma once
+
+#include "common.hpp"
+
+namespace mtpv {
+
+template <int D>
+struct VRow;  // one lane's slice of a V row: D/16 bf16 values
+template <>
+struct VRow<128> {
+  uint4 v;
+};
+template <>
+struct VRow<64> {
+  uint2 v;
+};
+
+template <int D>
+__device__ __forceinline__ VRow<D> load_vrow(const uint16_t* p) {
+  VRow<D> r;
+  if constexpr (D == 128)
+    r.v = *reinterpret_cast<const uint4*>(p);
+  else
+    r.v = *reinterpret_cast<const uint2*>(p);
+  return r;
+}
+
+template <int D>
+__device__ __forceinline__ unsigned vrow_dword(const VRow<D>& r, int i) {
+  if constexpr (D == 128) {
+    return i == 0 ? r.v.x : i == 1 ? r.v.y : i == 2 ? r.v.z : r.v.w;
+  } else {
+    return i == 0 ? r.v.x : r.v.y;
+  }
+}
+
+// Operand A of the PV product for output column tile t: element t of each of
+// the lane's 8 V vectors, packed pairwise.
+template <int D, int T>
+__device__ __forceinline__ bf16x8 pack_v_operand(const VRow<D> (&vv)[8]) {
+  unsigned w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const unsigned x = vrow_dword<D>(vv[2 * j], T >> 1);
+    const unsigned y = vrow_dword<D>(vv[2 * j + 1], T >> 1);
+    w[j] = (T & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+  }
+  bf16x8 r;
+  __builtin_memcpy(&r, w, sizeof(r));
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+template <int D, int RB>
+struct MfmaState {
+  float m[RB];           // running row max (log2 domain), replicated over the 4 quarters
+  float l[RB];           // this lane's share of the running row sum
+  f32x4 acc[RB][D / 16];  // acc^T tiles
+};
+
+// One 32-key tile: scores, online-softmax update, PV accumulate.
+// kf: K operands of the two 16-key halves; vv: V vectors of keys
+// {4q..4q+3, 16+4q..16+4q+3}; vis(k, e) tells whether row tile k may see key
+// e of this lane's 8 keys.
+template <int D, int RB, typename VisFn>
+__device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
+                                          const bf16x8 (&kf)[2][D / 32],
+                                          const VRow<D> (&vv)[8], float scale_log2,
+                                          MfmaState<D, RB>& st, VisFn vis) {
+  constexpr int NC = D / 32;
+  constexpr int NT = D / 16;
+  bf16x8 pf[RB];
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NC; ++m) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][m], qf[k][m], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][m], qf[k][m], s1, 0, 0, 0);
+    }
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = s0[e] * scale_log2;
+      x[4 + e] = s1[e] * scale_log2;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!vis(k, e)) x[e] = neg_inf();
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(st.m[k], mx);
+    const float muse = mnew == neg_inf() ? 0.f : mnew;
+    const float alpha = fast_exp2(st.m[k] - muse);
+    float sum = 0.f;
+    __bf16 ph[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = fast_exp2(x[e] - muse);
+      sum += pe;
+      ph[e] = (__bf16)pe;
+    }
+    st.l[k] = st.l[k] * alpha + sum;
+    st.m[k] = mnew;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st.acc[k][t] *= alpha;
+    __builtin_memcpy(&pf[k], ph, sizeof(bf16x8));
+  }
+#define MTPV_PV_STEP(T)                                                                 \
+  if constexpr ((T) < NT) {                                                            \
+    const bf16x8 a = pack_v_operand<D, (T)>(vv);                                       \
+    _Pragma("unroll") for (int k = 0; k < RB; ++k) st.acc[k][(T)] =                    \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[k], st.acc[k][(T)], 0, 0, 0);     \
+  }
+  MTPV_PV_STEP(0)
+  MTPV_PV_STEP(1)
+  MTPV_PV_STEP(2)
+  MTPV_PV_STEP(3)
+  MTPV_PV_STEP(4)
+  MTPV_PV_STEP(5)
+  MTPV_PV_STEP(6)
+  MTPV_PV_STEP(7)
+#undef MTPV_PV_STEP
+}
+
+// Key index (0..31) inside a 32-key tile of this lane's e-th PV key.
+__device__ __forceinline__ int pv_key(int q, int e) { return e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4); }
+
+template <int D, int RB>
+__global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
+  constexpr int NC = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int VE = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int qd = lane >> 4;
+  const int b = blockIdx.y;
+  const Item it = decode_item(blockIdx.x * 4 + (threadIdx.x >> 6), p);
+  if (it.split >= p.max_splits) return;
+  const int L = p.ctx_lens[b];
+  if (L < 0 || L > p.max_ctx) return;  // reported by the combine
+  const int ns = num_splits(L, p.S);
+  if (it.split >= ns) return;
+  const int start = it.split * p.S;
+  const int end = min(L, start + p.S);
+  const bool last = it.split == ns - 1;
+
+  const uint16_t* qbase = static_cast<const uint16_t*>(p.q);
+  const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache) + (size_t)it.kvh * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache) + (size_t)it.kvh * D;
+  const size_t slot_stride = (size_t)p.Hkv * D;
+
+  // Q^T operands of the RB row tiles.
+  bf16x8 qf[RB][NC];
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    const int rho = (it.rb * RB + k) * 16 + c;
+    if (rho < p.R) {
+      const int w = rho / p.g;
+      const int j = rho - w * p.g;
+      const uint16_t* src =
+          qbase + ((size_t)(b * p.W + w) * p.Hq + (size_t)it.kvh * p.g + j) * D + qd * 8;
+#pragma unroll
+      for (int m = 0; m < NC; ++m) qf[k][m] = load_bf16x8(src + m * 32);
+    } else {
+#pragma unroll
+      for (int m = 0; m < NC; ++m) qf[k][m] = bf16x8{};
+    }
+  }
+
+  MfmaState<D, RB> st;
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    st.m[k] = neg_inf();
+    st.l[k] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Committed keys [start, end), 32 per step (two pages; start is a multiple of 32).
+  const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
+  bool bad = false;
+  for (int t0 = start; t0 < end; t0 += 32) {
+    const int nk = end - t0;  // keys of this tile that are committed (may exceed 32)
+    int pg0 = btrow[t0 >> 4];
+    int pg1 = nk > 16 ? btrow[(t0 >> 4) + 1] : pg0;
+    if ((unsigned)pg0 >= (unsigned)p.num_pages) {
+      bad = true;
+      pg0 = 0;
+    }
+    if ((unsigned)pg1 >= (unsigned)p.num_pages) {
+      bad = true;
+      pg1 = 0;
+    }
+    // Keys past the committed range load the tile's first row (always valid)
+    // and are masked out of the softmax.
+    bf16x8 kf[2][NC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = kt * 16 + c;
+      const bool v = key < nk;
+      const int pg = v ? (kt ? pg1 : pg0) : pg0;
+      const int slot = v ? c : 0;
+      const uint16_t* src = kc + ((size_t)pg * kPage + slot) * slot_stride + qd * 8;
+#pragma unroll
+      for (int m = 0; m < NC; ++m) kf[kt][m] = load_bf16x8(src + m * 32);
+    }
+    VRow<D> vv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = pv_key(qd, e);
+      const bool v = key < nk;
+      const int pg = v ? (e < 4 ? pg0 : pg1) : pg0;
+      const int slot = v ? (key & 15) : 0;
+      vv[e] = load_vrow<D>(vc + ((size_t)pg * kPage + slot) * slot_stride + c * VE);
+    }
+    if (nk >= 32) {
+      mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [](int, int) { return true; });
+    } else {
+      mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st,
+                       [&](int, int e) { return (e < 4 ? 4 * qd + e : 16 + 4 * qd + e - 4) < nk; });
+    }
+  }
+
+  // In-block keys (the block's own K/V), masked per row, in the last split.
+  if (last) {
+    bool ok;
+    const uint64_t vnode =
+        node_visibility(p.mask_kind[b], p.mask_ids + (size_t)b * p.W, p.W, p.lookback, lane, ok);
+    if (ok) {
+      uint64_t vrow[RB];
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        const int rho = min((it.rb * RB + k) * 16 + c, p.R - 1);
+        vrow[k] = shfl64(vnode, rho / p.g);
+      }
+      const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (size_t)it.kvh * D;
+      const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (size_t)it.kvh * D;
+      for (int j0 = 0; j0 < p.W; j0 += 32) {
+        bf16x8 kf[2][NC];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          int j = j0 + kt * 16 + c;
+          j = j < p.W ? j : 0;
+          const uint16_t* src = kn + (size_t)(b * p.W + j) * slot_stride + qd * 8;
+#pragma unroll
+          for (int m = 0; m < NC; ++m) kf[kt][m] = load_bf16x8(src + m * 32);
+        }
+        VRow<D> vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          int j = j0 + pv_key(qd, e);
+          j = j < p.W ? j : 0;
+          vv[e] = load_vrow<D>(vn + (size_t)(b * p.W + j) * slot_stride + c * VE);
+        }
+        // Bits >= W of a visibility row are zero, so padded keys are masked.
+        mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [&](int k, int e) {
+          const int j = j0 + (e < 4 ? 4 * qd + e : 16 + 4 * qd + e - 4);
+          return ((vrow[k] >> j) & 1ull) != 0ull;
+        });
+      }
+    }
+  }
+
+  if (bad) {
+    if (lane == 0) raise_status(MTP_DEV_BAD_PAGE);
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      st.m[k] = qnan();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{qnan(), qnan(), qnan(), qnan()};
+    }
+  }
+
+  // Store the partial (m, l, unnormalised acc) of every real row.
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    float l = st.l[k];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int rho = (it.rb * RB + k) * 16 + c;
+    if (rho < p.R) {
+      const size_t pidx =
+          (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R + rho;
+      if (qd == 0) {
+        p.part_ml[2 * pidx] = st.m[k];
+        p.part_ml[2 * pidx + 1] = l;
+      }
+      float* dst = p.part_acc + pidx * D + qd * (D / 4);
+      // lane holds d = qd*D/4 + e*(D/16) + t in acc[k][t][e]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int t = 0; t < NT; t += 4) {
+          float4 v;
+          v.x = st.acc[k][t][e];
+          v.y = st.acc[k][t + 1][e];
+          v.z = st.acc[k][t + 2][e];
+          v.w = st.acc[k][t + 3][e];
+          *reinterpret_cast<float4*>(dst + e * (D / 16) + t) = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace mtpv

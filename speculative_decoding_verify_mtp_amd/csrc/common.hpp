@@ -1,0 +1,148 @@
+// Shared device helpers of the verify-step kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mtp_verify.h"
+
+namespace mtpv {
+
+constexpr int kPage = MTP_PAGE_SIZE;
+constexpr int kWave = 64;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Per-device sticky status word (MTP_DEV_* bits).  Kernels OR bits into it
+// with a global atomic; the host reads it with hipMemcpyFromSymbol.
+__device__ unsigned int g_status;
+
+__device__ __forceinline__ void raise_status(unsigned bits) { atomicOr(&g_status, bits); }
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+__device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
+
+// 2^x on the transcendental unit; exact 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+  const unsigned lo = __shfl((unsigned)v, src);
+  const unsigned hi = __shfl((unsigned)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
+  return __uint_as_float((unsigned)h << 16);
+}
+
+// In-block visibility of block node `lane` as a W-bit row (bit j set when the
+// node may attend to block row j); lanes >= W return 0.  Every lane of the
+// wave must be active.  `ok` (wave-uniform) reports whether the mask
+// description is well formed.
+//  CHAIN   : rows 0..i (the AR-causal verifier mask).
+//  TREE    : the node and its ancestors; the ancestor closure is built by
+//            pointer jumping, 6 rounds cover any depth below 64.
+//  SEGMENT : own-segment rows up to i, plus rows of the `lookback` previous
+//            segments (all earlier segments when lookback < 0).
+__device__ inline uint64_t node_visibility(int kind, const int32_t* ids, int W, int lookback,
+                                           int lane, bool& ok) {
+  const bool in = lane < W;
+  if (kind == MTP_MASK_CHAIN) {
+    ok = true;
+    return in ? (~0ull >> (63 - lane)) : 0ull;
+  }
+  const int id = in ? ids[lane] : 0;
+  if (kind == MTP_MASK_TREE) {
+    const bool bad = in && lane >= 1 && (id < 0 || id >= lane);
+    ok = __ballot(bad) == 0ull;
+    if (!ok) return 0ull;
+    int up = (in && lane >= 1) ? id : lane;
+    uint64_t anc = in ? ((1ull << lane) | (lane >= 1 ? (1ull << id) : 0ull)) : 0ull;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+      anc |= shfl64(anc, up);
+      up = __shfl(up, up);
+    }
+    return anc;
+  }
+  if (kind == MTP_MASK_SEGMENT) {
+    const int prev = __shfl(id, lane > 0 ? lane - 1 : 0);
+    const int step = id - prev;
+    const bool bad = in && (lane == 0 ? id != 0 : (step != 0 && step != 1));
+    ok = __ballot(bad) == 0ull;
+    if (!ok) return 0ull;
+    uint64_t vis = 0;
+    for (int j = 0; j < W; ++j) {
+      const int sj = __shfl(id, j);
+      const bool v = (sj == id && j <= lane) || (sj < id && (lookback < 0 || id - sj <= lookback));
+      vis |= (uint64_t)v << j;
+    }
+    return in ? vis : 0ull;
+  }
+  ok = false;
+  return 0ull;
+}
+
+// Arguments of the attention kernels (split-K partials + combine).
+struct AttnParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const void* k_new;
+  const void* v_new;
+  const uint8_t* mask_kind;
+  const int32_t* mask_ids;
+  float* part_acc;  // [B, max_splits, Hkv, R, D]
+  float* part_ml;   // [B, max_splits, Hkv, R, 2]: running max (log2 domain), sum
+  float* out;       // [B, W, Hq, D]
+  float* lse;       // [B, W, Hq] or null
+  int B, W, Hq, Hkv, g, R;
+  int nRB;         // row blocks per (sequence, KV head)
+  int S;           // committed tokens per split (multiple of 32)
+  int max_splits;  // max(1, ceil(max_ctx / S))
+  int max_pages, num_pages, max_ctx, lookback;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+// Work item of the split-K kernels: (row block, KV head, split) of sequence
+// blockIdx.y, row block fastest so that the waves of one workgroup read
+// neighbouring KV rows.
+struct Item {
+  int rb, kvh, split;
+};
+
+__device__ __forceinline__ Item decode_item(int item, const AttnParams& p) {
+  Item it;
+  it.rb = item % p.nRB;
+  const int t = item / p.nRB;
+  it.kvh = t % p.Hkv;
+  it.split = t / p.Hkv;
+  return it;
+}
+
+__device__ __forceinline__ int num_splits(int L, int S) { return L > 0 ? (L + S - 1) / S : 1; }
+
+}  // namespace mtpv

@@ -1,0 +1,340 @@
+// Host side of libmtpverify: argument validation, split-K planning and
+// kernel launches for the C ABI declared in include/mtp_verify.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "accept_commit.hpp"
+#include "attn_mfma.hpp"
+#include "attn_valu.hpp"
+#include "combine.hpp"
+#include "common.hpp"
+#include "mtp_verify.h"
+
+namespace {
+
+using namespace mtpv;
+
+// Committed tokens per split when the caller does not fix it: enough work
+// items to fill 256 CUs several times over, but no split shorter than 64 tokens
+// (the partial it writes would rival the K/V it reads) or longer than 2048.
+constexpr long kTargetItems = 2048;
+constexpr int kMinSplit = 64;
+constexpr int kMaxSplit = 2048;
+
+struct Plan {
+  bool mfma;       // bf16 with >= 16 rows per KV head
+  int g, R;        // group size, rows per KV head (W * g)
+  int RB;          // MFMA row tiles per wave (1, 2 or 4)
+  int nRB;         // row blocks (MFMA) or row chunks (VALU) per KV head
+  int S;           // committed tokens per split
+  int max_splits;  // splits of the longest context
+  size_t acc_bytes, ml_offset, ml_bytes;
+};
+
+mtp_status check_shape(const mtp_shape* s) {
+  if (s == nullptr) return MTP_ERR_NULL;
+  if (s->B < 0 || s->B > 65535) return MTP_ERR_SHAPE;
+  if (s->W < 1 || s->W > MTP_MAX_W) return MTP_ERR_SHAPE;
+  if (s->Hkv < 1 || s->Hq < 1 || s->Hq % s->Hkv != 0) return MTP_ERR_SHAPE;
+  if (s->num_pages < 0 || s->max_pages_per_seq < 0 || s->max_ctx_len < 0) return MTP_ERR_SHAPE;
+  if ((int64_t)s->max_ctx_len > (int64_t)s->max_pages_per_seq * MTP_PAGE_SIZE) return MTP_ERR_SHAPE;
+  if (s->max_ctx_len > 0 && s->num_pages < 1) return MTP_ERR_SHAPE;  // committed keys need pages
+  if (s->seg_lookback < -1) return MTP_ERR_SHAPE;
+  if (s->split_tokens < 0 || s->split_tokens % 32 != 0) return MTP_ERR_SHAPE;
+  if (!(s->scale >= 0.f) || isinf(s->scale)) return MTP_ERR_SHAPE;
+  if (s->page_size != MTP_PAGE_SIZE) return MTP_ERR_UNSUPPORTED;
+  if (s->D != 64 && s->D != 128) return MTP_ERR_UNSUPPORTED;
+  if (s->dtype != MTP_F32 && s->dtype != MTP_BF16) return MTP_ERR_UNSUPPORTED;
+  return MTP_OK;
+}
+
+int pow2_ceil(long x) {
+  int p = 1;
+  while (p < x && p < (1 << 30)) p <<= 1;
+  return p;
+}
+
+Plan make_plan(const mtp_shape& s) {
+  Plan pl;
+  pl.g = s.Hq / s.Hkv;
+  pl.R = s.W * pl.g;
+  pl.mfma = s.dtype == MTP_BF16 && pl.R >= 16;
+  if (pl.mfma) {
+    const int tiles = (pl.R + 15) / 16;
+    pl.RB = tiles >= 4 ? 4 : tiles;
+    pl.nRB = (tiles + pl.RB - 1) / pl.RB;
+  } else {
+    pl.RB = 0;
+    pl.nRB = (pl.R + kValuRows - 1) / kValuRows;
+  }
+  if (s.split_tokens > 0) {
+    pl.S = s.split_tokens;
+  } else {
+    const long work = (long)s.B * s.Hkv * pl.nRB * (long)(s.max_ctx_len > 0 ? s.max_ctx_len : 1);
+    int S = pow2_ceil((work + kTargetItems - 1) / kTargetItems);
+    pl.S = S < kMinSplit ? kMinSplit : (S > kMaxSplit ? kMaxSplit : S);
+  }
+  pl.max_splits = s.max_ctx_len > 0 ? (s.max_ctx_len + pl.S - 1) / pl.S : 1;
+  const size_t rows = (size_t)s.B * pl.max_splits * s.Hkv * pl.R;
+  pl.acc_bytes = rows * s.D * sizeof(float);
+  pl.ml_offset = (pl.acc_bytes + 255) & ~(size_t)255;
+  pl.ml_bytes = rows * 2 * sizeof(float);
+  return pl;
+}
+
+mtp_status launch_status() {
+  return hipGetLastError() == hipSuccess ? MTP_OK : MTP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mtp_abi_version(void) { return MTP_ABI_VERSION; }
+
+const char* mtp_status_string(int32_t status) {
+  switch (status) {
+    case MTP_OK: return "ok";
+    case MTP_ERR_NULL: return "a required pointer is NULL";
+    case MTP_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MTP_ERR_UNSUPPORTED: return "unsupported head dim, dtype or page size";
+    case MTP_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MTP_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+mtp_status mtp_verify_attn_workspace_size(const mtp_shape* shape, size_t* bytes) {
+  const mtp_status st = check_shape(shape);
+  if (st != MTP_OK) return st;
+  if (bytes == nullptr) return MTP_ERR_NULL;
+  const Plan pl = make_plan(*shape);
+  *bytes = pl.ml_offset + pl.ml_bytes;
+  return MTP_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+enum Phase { kPartial = 1, kCombine = 2, kBoth = 3 };
+
+mtp_status verify_attn_phases(int phases, const mtp_shape* shape, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens,
+                              const void* k_new, const void* v_new, const uint8_t* mask_kind,
+                              const int32_t* mask_ids, float* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const mtp_status st = check_shape(shape);
+  if (st != MTP_OK) return st;
+  const mtp_shape& s = *shape;
+  if (s.B == 0) return MTP_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !k_new || !v_new || !mask_kind ||
+      !mask_ids || !out || !workspace)
+    return MTP_ERR_NULL;
+  const Plan pl = make_plan(s);
+  if (workspace_bytes < pl.ml_offset + pl.ml_bytes || ((uintptr_t)workspace & 15) != 0)
+    return MTP_ERR_WORKSPACE;
+
+  AttnParams p;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.mask_kind = mask_kind;
+  p.mask_ids = mask_ids;
+  p.part_acc = static_cast<float*>(workspace);
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ml_offset);
+  p.out = out;
+  p.lse = lse;
+  p.B = s.B;
+  p.W = s.W;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = pl.g;
+  p.R = pl.R;
+  p.nRB = pl.nRB;
+  p.S = pl.S;
+  p.max_splits = pl.max_splits;
+  p.max_pages = s.max_pages_per_seq;
+  p.num_pages = s.num_pages;
+  p.max_ctx = s.max_ctx_len;
+  p.lookback = s.seg_lookback;
+  const float scale = s.scale > 0.f ? s.scale : 1.f / sqrtf((float)s.D);
+  p.scale_log2 = scale * kLog2e;
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  const dim3 block(256);
+  if (phases & kPartial) {
+    const long items = (long)pl.max_splits * s.Hkv * pl.nRB;
+    const dim3 grid((unsigned)((items + 3) / 4), (unsigned)s.B);
+    if (pl.mfma) {
+      if (s.D == 128) {
+        if (pl.RB == 4) attn_partial_mfma<128, 4><<<grid, block, 0, strm>>>(p);
+        else if (pl.RB == 2) attn_partial_mfma<128, 2><<<grid, block, 0, strm>>>(p);
+        else attn_partial_mfma<128, 1><<<grid, block, 0, strm>>>(p);
+      } else {
+        if (pl.RB == 4) attn_partial_mfma<64, 4><<<grid, block, 0, strm>>>(p);
+        else if (pl.RB == 2) attn_partial_mfma<64, 2><<<grid, block, 0, strm>>>(p);
+        else attn_partial_mfma<64, 1><<<grid, block, 0, strm>>>(p);
+      }
+    } else if (s.dtype == MTP_F32) {
+      if (s.D == 128) attn_partial_valu<float, 128><<<grid, block, 0, strm>>>(p);
+      else attn_partial_valu<float, 64><<<grid, block, 0, strm>>>(p);
+    } else {
+      if (s.D == 128) attn_partial_valu<uint16_t, 128><<<grid, block, 0, strm>>>(p);
+      else attn_partial_valu<uint16_t, 64><<<grid, block, 0, strm>>>(p);
+    }
+  }
+  if (phases & kCombine) {
+    const size_t rows = (size_t)s.B * s.W * s.Hq;
+    const dim3 cgrid((unsigned)((rows + 3) / 4));
+    if (s.D == 128) attn_combine<128><<<cgrid, block, 0, strm>>>(p);
+    else attn_combine<64><<<cgrid, block, 0, strm>>>(p);
+  }
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+#define MTPV_ATTN_ARGS                                                                       \
+  const mtp_shape *shape, const void *q, const void *k_cache, const void *v_cache,         \
+      const int32_t *block_table, const int32_t *ctx_lens, const void *k_new,              \
+      const void *v_new, const uint8_t *mask_kind, const int32_t *mask_ids, float *out,    \
+      float *lse, void *workspace, size_t workspace_bytes, void *stream
+#define MTPV_ATTN_PASS                                                                      \
+  shape, q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new, mask_kind, mask_ids, out, \
+      lse, workspace, workspace_bytes, stream
+
+mtp_status mtp_verify_attn(MTPV_ATTN_ARGS) { return verify_attn_phases(kBoth, MTPV_ATTN_PASS); }
+
+mtp_status mtp_verify_attn_partial(MTPV_ATTN_ARGS) {
+  return verify_attn_phases(kPartial, MTPV_ATTN_PASS);
+}
+
+mtp_status mtp_verify_attn_combine(MTPV_ATTN_ARGS) {
+  return verify_attn_phases(kCombine, MTPV_ATTN_PASS);
+}
+
+static mtp_status fill_accept(const mtp_shape* shape, const float* logits, int32_t V,
+                              const int32_t* draft_ids, const uint8_t* mask_kind,
+                              const int32_t* mask_ids, int32_t* accept_len, int32_t* accept_path,
+                              int32_t* bonus_id, AcceptParams& ap) {
+  if (shape == nullptr) return MTP_ERR_NULL;
+  if (shape->B < 0 || shape->W < 1 || shape->W > MTP_MAX_W || V < 1) return MTP_ERR_SHAPE;
+  if (shape->B > 0 && (!logits || !draft_ids || !mask_kind || !mask_ids || !accept_len ||
+                       !accept_path || !bonus_id))
+    return MTP_ERR_NULL;
+  ap.logits = logits;
+  ap.draft_ids = draft_ids;
+  ap.mask_kind = mask_kind;
+  ap.mask_ids = mask_ids;
+  ap.accept_len = accept_len;
+  ap.accept_path = accept_path;
+  ap.bonus_id = bonus_id;
+  ap.B = shape->B;
+  ap.W = shape->W;
+  ap.V = V;
+  return MTP_OK;
+}
+
+static mtp_status fill_commit(const mtp_shape* shape, const void* k_new, const void* v_new,
+                              const int32_t* accept_len, const int32_t* accept_path,
+                              const int32_t* block_table, const int32_t* ctx_lens_in,
+                              int32_t* ctx_lens_out, int32_t skip_root, void* k_cache,
+                              void* v_cache, bool fused, CommitParams& cp) {
+  const mtp_status st = check_shape(shape);
+  if (st != MTP_OK) return st;
+  if (shape->B > 0 &&
+      (!k_new || !v_new || !block_table || !ctx_lens_in || !ctx_lens_out || !k_cache || !v_cache ||
+       (!fused && (!accept_len || !accept_path))))
+    return MTP_ERR_NULL;
+  const int elem = shape->dtype == MTP_F32 ? 4 : 2;
+  cp.k_new = k_new;
+  cp.v_new = v_new;
+  cp.accept_len = accept_len;
+  cp.accept_path = accept_path;
+  cp.block_table = block_table;
+  cp.ctx_in = ctx_lens_in;
+  cp.ctx_out = ctx_lens_out;
+  cp.k_cache = k_cache;
+  cp.v_cache = v_cache;
+  cp.skip_root = skip_root ? 1 : 0;
+  cp.W = shape->W;
+  cp.max_pages = shape->max_pages_per_seq;
+  cp.num_pages = shape->num_pages;
+  cp.row_bytes = shape->Hkv * shape->D * elem;
+  return MTP_OK;
+}
+
+mtp_status mtp_accept(const mtp_shape* shape, const float* logits, int32_t V,
+                      const int32_t* draft_ids, const uint8_t* mask_kind,
+                      const int32_t* mask_ids, int32_t* accept_len, int32_t* accept_path,
+                      int32_t* bonus_id, void* stream) {
+  AcceptParams ap;
+  const mtp_status st = fill_accept(shape, logits, V, draft_ids, mask_kind, mask_ids, accept_len,
+                                    accept_path, bonus_id, ap);
+  if (st != MTP_OK || shape->B == 0) return st;
+  accept_kernel<<<dim3(shape->B), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(ap);
+  return launch_status();
+}
+
+mtp_status mtp_kv_commit(const mtp_shape* shape, const void* k_new, const void* v_new,
+                         const int32_t* accept_len, const int32_t* accept_path,
+                         const int32_t* block_table, const int32_t* ctx_lens_in,
+                         int32_t* ctx_lens_out, int32_t skip_root, void* k_cache,
+                         void* v_cache, void* stream) {
+  CommitParams cp;
+  const mtp_status st = fill_commit(shape, k_new, v_new, accept_len, accept_path, block_table,
+                                    ctx_lens_in, ctx_lens_out, skip_root, k_cache, v_cache, false,
+                                    cp);
+  if (st != MTP_OK || shape->B == 0) return st;
+  commit_kernel<<<dim3(shape->B), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(cp);
+  return launch_status();
+}
+
+mtp_status mtp_accept_commit(const mtp_shape* shape, const float* logits, int32_t V,
+                             const int32_t* draft_ids, const uint8_t* mask_kind,
+                             const int32_t* mask_ids, int32_t* accept_len,
+                             int32_t* accept_path, int32_t* bonus_id, const void* k_new,
+                             const void* v_new, const int32_t* block_table,
+                             const int32_t* ctx_lens_in, int32_t* ctx_lens_out,
+                             int32_t skip_root, void* k_cache, void* v_cache, void* stream) {
+  AcceptParams ap;
+  mtp_status st = fill_accept(shape, logits, V, draft_ids, mask_kind, mask_ids, accept_len,
+                              accept_path, bonus_id, ap);
+  if (st != MTP_OK) return st;
+  CommitParams cp;
+  st = fill_commit(shape, k_new, v_new, accept_len, accept_path, block_table, ctx_lens_in,
+                   ctx_lens_out, skip_root, k_cache, v_cache, true, cp);
+  if (st != MTP_OK || shape->B == 0) return st;
+  accept_commit_kernel<<<dim3(shape->B), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(ap, cp);
+  return launch_status();
+}
+
+mtp_status mtp_get_device_status(uint32_t* bits, int32_t clear) {
+  if (bits == nullptr) return MTP_ERR_NULL;
+  if (hipDeviceSynchronize() != hipSuccess) return MTP_ERR_HIP;
+  unsigned v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_status), sizeof(v), 0, hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return MTP_ERR_HIP;
+  *bits = v;
+  if (clear) {
+    const unsigned zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_status), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) !=
+        hipSuccess)
+      return MTP_ERR_HIP;
+  }
+  return MTP_OK;
+}
+
+}  // extern "C"

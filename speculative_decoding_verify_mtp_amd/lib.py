@@ -1,0 +1,261 @@
+"""Thin ctypes binding of libmtpverify.so (include/mtp_verify.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks their dtype / shape / contiguity, and passes raw
+device pointers plus the current HIP stream to the C ABI.  All computation
+happens in the library's HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmtpverify.so")
+
+MTP_F32, MTP_BF16 = 0, 1
+MASK_CHAIN, MASK_TREE, MASK_SEGMENT = 0, 1, 2
+DEV_BAD_MASK, DEV_BAD_CTX, DEV_BAD_PAGE, DEV_BAD_ACCEPT = 1, 2, 4, 8
+
+EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_size",
+           "mtp_verify_attn", "mtp_verify_attn_partial", "mtp_verify_attn_combine",
+           "mtp_accept", "mtp_kv_commit", "mtp_accept_commit", "mtp_get_device_status")
+_ATTN_FN = {"both": "mtp_verify_attn", "partial": "mtp_verify_attn_partial",
+            "combine": "mtp_verify_attn_combine"}
+
+
+class MtpError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: status {status} ({text})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("W", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("max_ctx_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("seg_lookback", ctypes.c_int32),
+                ("split_tokens", ctypes.c_int32)]
+
+
+_lib = None
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+def load() -> ctypes.CDLL:
+    """Loads the library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m speculative_decoding_verify_mtp_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sp = ctypes.POINTER(Shape)
+    lib.mtp_abi_version.restype = _i32
+    lib.mtp_abi_version.argtypes = []
+    lib.mtp_status_string.restype = ctypes.c_char_p
+    lib.mtp_status_string.argtypes = [_i32]
+    lib.mtp_verify_attn_workspace_size.restype = _i32
+    lib.mtp_verify_attn_workspace_size.argtypes = [sp, ctypes.POINTER(_sz)]
+    for fn in _ATTN_FN.values():
+        getattr(lib, fn).restype = _i32
+        getattr(lib, fn).argtypes = [sp] + [_vp] * 11 + [_vp, _sz, _vp]
+    lib.mtp_accept.restype = _i32
+    lib.mtp_accept.argtypes = [sp, _vp, _i32] + [_vp] * 6 + [_vp]
+    lib.mtp_kv_commit.restype = _i32
+    lib.mtp_kv_commit.argtypes = [sp] + [_vp] * 7 + [_i32, _vp, _vp, _vp]
+    lib.mtp_accept_commit.restype = _i32
+    lib.mtp_accept_commit.argtypes = ([sp, _vp, _i32] + [_vp] * 6 + [_vp] * 5
+                                      + [_i32, _vp, _vp, _vp])
+    lib.mtp_get_device_status.restype = _i32
+    lib.mtp_get_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i32]
+    if lib.mtp_abi_version() != 1:
+        raise RuntimeError("libmtpverify ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MtpError(fn, status, load().mtp_status_string(status).decode())
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmtpverify must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MTP_F32
+    if t.dtype == torch.bfloat16:
+        return MTP_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+@dataclass
+class VerifyShape:
+    """Python mirror of mtp_shape."""
+
+    B: int
+    W: int
+    Hq: int
+    Hkv: int
+    D: int
+    num_pages: int
+    max_pages_per_seq: int
+    max_ctx_len: int
+    dtype: int
+    scale: float = 0.0
+    seg_lookback: int = -1
+    split_tokens: int = 0
+
+    def c(self) -> Shape:
+        return Shape(self.B, self.W, self.Hq, self.Hkv, self.D, 16, self.num_pages,
+                     self.max_pages_per_seq, self.max_ctx_len, self.dtype, self.scale,
+                     self.seg_lookback, self.split_tokens)
+
+
+def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor, *,
+             max_ctx_len: int | None = None, scale: float = 0.0, seg_lookback: int = -1,
+             split_tokens: int = 0) -> VerifyShape:
+    B, W, Hq, D = q.shape
+    num_pages, page, Hkv, D2 = k_cache.shape
+    if page != 16 or D2 != D:
+        raise ValueError("k_cache must be [num_pages, 16, Hkv, D]")
+    maxp = block_table.shape[1]
+    return VerifyShape(B, W, Hq, Hkv, D, num_pages, maxp,
+                       maxp * 16 if max_ctx_len is None else int(max_ctx_len),
+                       _dtype_code(q), float(scale), int(seg_lookback), int(split_tokens))
+
+
+def workspace_bytes(shape: VerifyShape) -> int:
+    n = ctypes.c_size_t(0)
+    cs = shape.c()
+    _check("mtp_verify_attn_workspace_size",
+           load().mtp_verify_attn_workspace_size(ctypes.byref(cs), ctypes.byref(n)))
+    return int(n.value)
+
+
+def verify_attn(q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new, mask_kind, mask_ids,
+                *, out=None, lse=None, want_lse=True, workspace=None, shape=None,
+                max_ctx_len=None, scale=0.0, seg_lookback=-1, split_tokens=0, stream=None,
+                phase="both"):
+    """Verify attention; returns (out [B,W,Hq,D] fp32, lse [B,W,Hq] fp32 or None).
+
+    phase "partial" / "combine" launches only one of the two kernels (the
+    combine must follow a partial launch on the same workspace)."""
+    lib = load()
+    if shape is None:
+        shape = shape_of(q, k_cache, block_table, max_ctx_len=max_ctx_len, scale=scale,
+                         seg_lookback=seg_lookback, split_tokens=split_tokens)
+    B, W, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, W, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, W, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(shape), 16), dtype=torch.uint8,
+                                device=q.device)
+    for t in (block_table, ctx_lens, mask_ids):
+        if t.dtype != torch.int32:
+            raise ValueError("block_table, ctx_lens and mask_ids must be int32")
+    if mask_kind.dtype != torch.uint8:
+        raise ValueError("mask_kind must be uint8")
+    cs = shape.c()
+    fn = _ATTN_FN[phase]
+    _check(fn, getattr(lib, fn)(
+        ctypes.byref(cs), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(ctx_lens), _ptr(k_new), _ptr(v_new), _ptr(mask_kind), _ptr(mask_ids), _ptr(out),
+        _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def _accept_shape(draft_ids: torch.Tensor) -> Shape:
+    B, W = draft_ids.shape
+    return Shape(B, W, 1, 1, 64, 16, 0, 0, 0, MTP_F32, 0.0, -1, 0)
+
+
+def accept(logits, draft_ids, mask_kind, mask_ids, *, accept_len=None, accept_path=None,
+           bonus_id=None, stream=None):
+    """Greedy acceptance; returns (accept_len [B], accept_path [B,W], bonus_id [B]) int32."""
+    lib = load()
+    B, W, V = logits.shape
+    dev = logits.device
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    accept_path = (torch.empty((B, W), dtype=torch.int32, device=dev) if accept_path is None
+                   else accept_path)
+    bonus_id = torch.empty(B, dtype=torch.int32, device=dev) if bonus_id is None else bonus_id
+    cs = _accept_shape(draft_ids)
+    _check("mtp_accept", lib.mtp_accept(
+        ctypes.byref(cs), _ptr(logits), V, _ptr(draft_ids), _ptr(mask_kind), _ptr(mask_ids),
+        _ptr(accept_len), _ptr(accept_path), _ptr(bonus_id), _stream(stream)))
+    return accept_len, accept_path, bonus_id
+
+
+def _commit_shape(k_new, k_cache, block_table) -> Shape:
+    B, W, Hkv, D = k_new.shape
+    maxp = block_table.shape[1]
+    return Shape(B, W, Hkv, Hkv, D, 16, k_cache.shape[0], maxp, 0, _dtype_code(k_new), 0.0, -1, 0)
+
+
+def kv_commit(k_new, v_new, accept_len, accept_path, block_table, ctx_lens_in, k_cache, v_cache,
+              *, ctx_lens_out=None, skip_root=False, stream=None):
+    """Writes the accepted rows into the cache (in place); returns ctx_lens_out."""
+    lib = load()
+    if ctx_lens_out is None:
+        ctx_lens_out = torch.empty_like(ctx_lens_in)
+    cs = _commit_shape(k_new, k_cache, block_table)
+    _check("mtp_kv_commit", lib.mtp_kv_commit(
+        ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(accept_len), _ptr(accept_path),
+        _ptr(block_table), _ptr(ctx_lens_in), _ptr(ctx_lens_out), int(bool(skip_root)),
+        _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+    return ctx_lens_out
+
+
+def accept_commit(logits, draft_ids, mask_kind, mask_ids, k_new, v_new, block_table, ctx_lens_in,
+                  k_cache, v_cache, *, accept_len=None, accept_path=None, bonus_id=None,
+                  ctx_lens_out=None, skip_root=False, stream=None):
+    """Fused acceptance + commit; returns (accept_len, accept_path, bonus_id, ctx_lens_out)."""
+    lib = load()
+    B, W, V = logits.shape
+    dev = logits.device
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    accept_path = (torch.empty((B, W), dtype=torch.int32, device=dev) if accept_path is None
+                   else accept_path)
+    bonus_id = torch.empty(B, dtype=torch.int32, device=dev) if bonus_id is None else bonus_id
+    if ctx_lens_out is None:
+        ctx_lens_out = torch.empty_like(ctx_lens_in)
+    cs = _commit_shape(k_new, k_cache, block_table)
+    _check("mtp_accept_commit", lib.mtp_accept_commit(
+        ctypes.byref(cs), _ptr(logits), V, _ptr(draft_ids), _ptr(mask_kind), _ptr(mask_ids),
+        _ptr(accept_len), _ptr(accept_path), _ptr(bonus_id), _ptr(k_new), _ptr(v_new),
+        _ptr(block_table), _ptr(ctx_lens_in), _ptr(ctx_lens_out), int(bool(skip_root)),
+        _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+    return accept_len, accept_path, bonus_id, ctx_lens_out
+
+
+def device_status(clear: bool = True) -> int:
+    """Sticky device status bits (MTP_DEV_*); synchronises the device."""
+    v = ctypes.c_uint32(0)
+    _check("mtp_get_device_status", load().mtp_get_device_status(ctypes.byref(v), int(clear)))
+    return int(v.value)
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

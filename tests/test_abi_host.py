@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI that need no GPU: the library builds and
+loads, exports every function include/mtp_verify.h declares, reports
+argument errors without touching the device, and sizes its workspace by
+the documented split plan."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decoding_verify_mtp_amd import build as B
+from speculative_decoding_verify_mtp_amd import lib
+
+HEADER = os.path.join(B.ROOT, "include", "mtp_verify.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB):
+        B.build()
+    return lib.load()
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert declared_functions() == sorted(lib.EXPORTS)
+
+
+def test_library_exports_every_declared_function(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {B.LIB}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), f"{name} not exported with C linkage"
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.mtp_abi_version() == 1
+    for code in range(6):
+        assert L.mtp_status_string(code).decode()
+    assert L.mtp_status_string(99).decode() == "unknown status"
+
+
+def shape(**kw) -> lib.Shape:
+    base = dict(B=2, W=8, Hq=8, Hkv=2, D=128, num_pages=100, max_pages_per_seq=40,
+                max_ctx_len=600, dtype=lib.MTP_BF16)
+    base.update(kw)
+    return lib.VerifyShape(**base).c()
+
+
+def ws(L, s) -> tuple[int, int]:
+    n = ctypes.c_size_t(0)
+    st = L.mtp_verify_attn_workspace_size(ctypes.byref(s), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(W=0), 2), (dict(W=65), 2), (dict(Hq=6, Hkv=4), 2), (dict(Hkv=0), 2),
+    (dict(D=96), 3), (dict(dtype=5), 3), (dict(max_ctx_len=641), 2), (dict(B=-1), 2),
+    (dict(seg_lookback=-2), 2), (dict(split_tokens=48), 2), (dict(scale=-1.0), 2),
+    (dict(scale=float("nan")), 2), (dict(num_pages=-1), 2), (dict(num_pages=0), 2),
+])
+def test_shape_errors_are_reported_on_the_host(L, bad, code):
+    s = shape(**bad)
+    assert ws(L, s)[0] == code
+    # the same error from the launch entry point, before any pointer is looked at
+    assert L.mtp_verify_attn(ctypes.byref(s), *([None] * 11), None, 0, None) == code
+
+
+def test_page_size_must_be_16(L):
+    s = shape()
+    s.page_size = 32
+    assert ws(L, s)[0] == 3
+
+
+def test_null_pointers_and_small_workspace(L):
+    s = shape()
+    assert L.mtp_verify_attn(ctypes.byref(s), *([None] * 11), None, 0, None) == 1
+    assert L.mtp_verify_attn_workspace_size(None, None) == 1
+    assert L.mtp_accept(None, None, 10, *([None] * 6), None) == 1
+    fake = ctypes.c_void_p(16)  # never dereferenced: the size check fails first
+    st = L.mtp_verify_attn(ctypes.byref(s), *([fake] * 10), None, fake, 8, None)
+    assert st == 4
+    bad = ctypes.c_void_p(18)  # misaligned
+    need = ws(L, s)[1]
+    assert L.mtp_verify_attn(ctypes.byref(s), *([fake] * 10), None, bad, need, None) == 4
+    assert L.mtp_accept(ctypes.byref(s), fake, 0, *([fake] * 6), None) == 2
+
+
+def test_empty_batch_needs_no_pointers(L):
+    s = shape(B=0)
+    assert L.mtp_verify_attn(ctypes.byref(s), *([None] * 11), None, 0, None) == 0
+    assert L.mtp_accept(ctypes.byref(s), None, 10, *([None] * 6), None) == 0
+    assert L.mtp_kv_commit(ctypes.byref(s), *([None] * 7), 0, None, None, None) == 0
+
+
+def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
+    """The documented split plan: rows per KV head R = W * g; bf16 with R >= 16
+    runs on MFMA in row blocks of up to 64 rows, everything else in chunks of
+    4 rows; the automatic split is the power of two giving about 2048 work
+    items, clamped to [64, 2048] tokens."""
+    g = Hq // Hkv
+    R = W * g
+    if dtype == lib.MTP_BF16 and R >= 16:
+        tiles = (R + 15) // 16
+        rb = min(4, tiles)
+        nrb = (tiles + rb - 1) // rb
+    else:
+        nrb = (R + 3) // 4
+    if split == 0:
+        work = B * Hkv * nrb * max(max_ctx, 1)
+        target = -(-work // 2048)
+        S = 1
+        while S < target:
+            S *= 2
+        S = min(max(S, 64), 2048)
+    else:
+        S = split
+    ns = -(-max_ctx // S) if max_ctx > 0 else 1
+    rows = B * ns * Hkv * R
+    acc = rows * D * 4
+    return ((acc + 255) // 256) * 256 + rows * 8
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=1, W=8, Hq=20, Hkv=5, D=128, dtype=1, max_ctx=4096),
+    dict(B=1, W=32, Hq=32, Hkv=8, D=128, dtype=1, max_ctx=8192),
+    dict(B=4, W=16, Hq=16, Hkv=16, D=64, dtype=1, max_ctx=16384),
+    dict(B=64, W=16, Hq=32, Hkv=8, D=128, dtype=1, max_ctx=32768),
+    dict(B=1, W=4, Hq=4, Hkv=4, D=64, dtype=0, max_ctx=256),
+    dict(B=3, W=3, Hq=4, Hkv=4, D=128, dtype=1, max_ctx=0),
+    dict(B=2, W=8, Hq=8, Hkv=2, D=128, dtype=1, max_ctx=600, split=96),
+])
+def test_workspace_follows_the_split_plan(L, kw):
+    s = lib.VerifyShape(kw["B"], kw["W"], kw["Hq"], kw["Hkv"], kw["D"], 10,
+                        max(1, -(-kw["max_ctx"] // 16)), kw["max_ctx"], kw["dtype"],
+                        split_tokens=kw.get("split", 0)).c()
+    st, n = ws(L, s)
+    assert st == 0
+    assert n == expected_workspace(kw["B"], kw["W"], kw["Hq"], kw["Hkv"], kw["D"], kw["dtype"],
+                                   kw["max_ctx"], kw.get("split", 0))
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(lib, "_lib", None)
+    monkeypatch.setattr(lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        lib.load()

@@ -1,0 +1,321 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Attention within |d| <= 1e-3 + 1e-2 |ref| elementwise (bf16 inputs) or
+1e-4 + 1e-4 |ref| (fp32 inputs); acceptance, paths, bonus ids, context
+lengths and committed K/V bytes bit-exact.  Small cases span several 32-key
+tiles, several splits and ragged tails; the five full-size workloads run in
+the launch configuration the benchmark uses (sampled sequences for the
+ragged batch).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_common import (I, O, lib, assert_accept_equal, assert_attn_close, banner, f64,
+                              gpu_inputs, ints, oracle_accept, oracle_attn, oracle_attn_sub, raw,
+                              run_attn, sub_problem, tol_for)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.filterwarnings("ignore::RuntimeWarning"),
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def W_(name, **kw) -> I.Workload:
+    base = dict(name=name, B=2, Hq=8, Hkv=2, D=128, W=8, dtype="bf16", ctx_lo=100, ctx_hi=700,
+                masks="chain")
+    base.update(kw)
+    return I.Workload(**base)
+
+
+SMALL = [
+    I.WORKLOADS["tiny_chain"],
+    W_("chain_g4", Hq=20, Hkv=5, W=8, ctx_lo=300, ctx_hi=700),
+    W_("tree_w32", Hq=32, Hkv=8, W=32, ctx_lo=500, ctx_hi=1100, masks="tree"),
+    W_("segment_all", Hq=16, Hkv=16, D=64, W=16, ctx_lo=200, ctx_hi=600, masks="segment"),
+    W_("segment_lca", Hq=16, Hkv=16, D=64, W=16, ctx_lo=200, ctx_hi=600, masks="segment",
+       seg_lookback=1),
+    W_("segment_own", Hq=4, Hkv=1, D=64, W=20, ctx_lo=0, ctx_hi=90, masks="segment",
+       seg_lookback=0),
+    W_("mixed_b6", B=6, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=900, masks="mixed"),
+    W_("valu_bf16_r3", Hq=4, Hkv=4, W=3, ctx_lo=50, ctx_hi=333, masks="tree"),
+    W_("valu_bf16_d64", Hq=6, Hkv=3, D=64, W=7, ctx_lo=17, ctx_hi=81, masks="mixed"),
+    W_("fp32_d128_tree", Hq=8, Hkv=2, W=5, dtype="f32", ctx_lo=40, ctx_hi=300, masks="tree"),
+    W_("fp32_d64_seg", Hq=3, Hkv=1, D=64, W=9, dtype="f32", ctx_lo=0, ctx_hi=64,
+       masks="segment", seg_lookback=1),
+    W_("w1_decode", B=3, Hq=16, Hkv=2, W=1, ctx_lo=1, ctx_hi=500),
+    W_("w1_decode_d64", B=3, Hq=32, Hkv=2, D=64, W=1, ctx_lo=0, ctx_hi=200),
+    W_("w64_tree", Hq=4, Hkv=2, W=64, ctx_lo=90, ctx_hi=400, masks="tree", tree_depth=63),
+    W_("w64_chain_d64", Hq=2, Hkv=2, D=64, W=64, ctx_lo=1, ctx_hi=130),
+    W_("w33_mixed_g8", B=3, Hq=64, Hkv=8, W=33, ctx_lo=31, ctx_hi=97, masks="mixed"),
+    W_("ctx0", B=3, Hq=8, Hkv=8, W=16, ctx_lo=0, ctx_hi=0, masks="mixed"),
+    W_("ctx_page_edges", B=4, Hq=8, Hkv=1, W=4, ctx_lo=15, ctx_hi=17),
+    W_("mask_tokens", Hq=16, Hkv=4, W=12, ctx_lo=64, ctx_hi=64, mask_token_rows=4),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_attention_matches_oracle_small(wl):
+    inp = gpu_inputs(wl, 7)
+    out, lse = run_attn(inp)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
+
+
+@pytest.mark.parametrize("split", [32, 64, 96, 2048])
+def test_split_size_does_not_change_the_result(split):
+    wl = W_("splits", B=3, Hq=16, Hkv=4, W=8, ctx_lo=1, ctx_hi=700, masks="mixed")
+    inp = gpu_inputs(wl, 3)
+    out, lse = run_attn(inp, split_tokens=split)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"split {split}")
+
+
+def test_loose_max_ctx_len_bound():
+    """max_ctx_len only sizes the split plan; a loose bound gives the same result."""
+    wl = W_("loose", B=2, Hq=8, Hkv=2, W=8, ctx_lo=10, ctx_hi=300, masks="tree")
+    inp = gpu_inputs(wl, 4)
+    out, lse = run_attn(inp, max_ctx_len=inp["block_table"].shape[1] * 16)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl))
+
+
+FULL = ["tiny_chain", "bitnet2b_chain", "llama3_8b_tree", "lca_segments"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workloads(name):
+    wl = I.WORKLOADS[name]
+    inp = gpu_inputs(wl, I.workload_seed(name))
+    out, lse = run_attn(inp)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=name)
+    assert_accept_equal(lib.accept(inp["logits"], inp["draft_ids"], inp["mask_kind"],
+                                   inp["mask_ids"]), oracle_accept(inp))
+
+
+def test_full_size_lca_with_fig2_lookback():
+    wl = I.WORKLOADS["lca_segments"].scaled(seg_lookback=1)
+    inp = gpu_inputs(wl, I.workload_seed("lca_segments"))
+    out, lse = run_attn(inp)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what="lca lookback 1")
+
+
+def test_full_size_ragged_batch_sampled():
+    name = "ragged_batch"
+    wl = I.WORKLOADS[name]
+    inp = gpu_inputs(wl, I.workload_seed(name))
+    out, lse = run_attn(inp)
+    ctx = inp["host"]["ctx_lens"]
+    # the longest and shortest sequence, plus a chain and a tree from the middle
+    seqs = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 10, 21})
+    banner(f"ragged sample {seqs} ctx={[int(ctx[s]) for s in seqs]}")
+    sub = sub_problem(inp, seqs)
+    ref_out, ref_lse = oracle_attn_sub(sub)
+    sel = torch.tensor(seqs, device=out.device)
+    assert_attn_close(out[sel], lse[sel], ref_out, ref_lse, *tol_for(wl), what=name)
+    assert_accept_equal(lib.accept(inp["logits"], inp["draft_ids"], inp["mask_kind"],
+                                   inp["mask_ids"]), oracle_accept(inp))
+
+
+# ----------------------------------------------------------------------------
+# acceptance
+# ----------------------------------------------------------------------------
+
+ACCEPT = [
+    W_("acc_chain", B=16, W=8, ctx_lo=1, ctx_hi=1),
+    W_("acc_tree", B=16, W=32, ctx_lo=1, ctx_hi=1, masks="tree"),
+    W_("acc_tree_w64", B=8, W=64, ctx_lo=1, ctx_hi=1, masks="tree", tree_depth=63, match_p=0.9),
+    W_("acc_segment", B=16, W=16, ctx_lo=1, ctx_hi=1, masks="segment"),
+    W_("acc_mixed_v7", B=16, W=16, ctx_lo=1, ctx_hi=1, masks="mixed", vocab=7),
+    W_("acc_reject_all", B=8, W=16, ctx_lo=1, ctx_hi=1, masks="mixed", match_p=0.0),
+    W_("acc_accept_all", B=8, W=16, ctx_lo=1, ctx_hi=1, masks="chain", match_p=1.0),
+    W_("acc_mask_tokens", B=8, W=12, ctx_lo=1, ctx_hi=1, masks="chain", match_p=1.0,
+       mask_token_rows=5),
+    W_("acc_w1", B=4, W=1, ctx_lo=1, ctx_hi=1),
+    W_("acc_vocab_big", B=2, W=8, ctx_lo=1, ctx_hi=1, vocab=50000),
+]
+
+
+@pytest.mark.parametrize("wl", ACCEPT, ids=[w.name for w in ACCEPT])
+def test_accept_bit_exact(wl):
+    inp = gpu_inputs(wl.scaled(D=64, Hq=2, Hkv=2), 11)
+    got = lib.accept(inp["logits"], inp["draft_ids"], inp["mask_kind"], inp["mask_ids"])
+    assert_accept_equal(got, oracle_accept(inp))
+
+
+def test_accept_argmax_ties_take_the_smallest_id():
+    B, W, V = 3, 4, 300
+    logits = torch.zeros((B, W, V), dtype=torch.float32)
+    tgt = np.array([[5, 299, 0, 77], [64, 128, 192, 256], [1, 2, 3, 4]])
+    for b in range(B):
+        for i in range(W):
+            logits[b, i, tgt[b, i]] = 2.0
+            logits[b, i, tgt[b, i] + 1:][::7] = 2.0  # later ids tie with it
+    draft = torch.tensor([[-1, 5, 299, 0], [-1, 64, 7, 192], [-1, 1, 2, 3]], dtype=torch.int32)
+    kinds = torch.zeros(B, dtype=torch.uint8)
+    ids = torch.tensor(np.tile(np.arange(-1, W - 1), (B, 1)), dtype=torch.int32)
+    ref = O.accept(logits.numpy(), draft.numpy(), kinds.numpy(), ids.numpy())
+    got = lib.accept(logits.cuda(), draft.cuda(), kinds.cuda(), ids.cuda())
+    assert_accept_equal(got, ref)
+    assert list(ints(got[0])) == [3, 1, 3]
+
+
+# ----------------------------------------------------------------------------
+# commit
+# ----------------------------------------------------------------------------
+
+COMMIT = [
+    W_("com_mixed", B=6, Hq=8, Hkv=2, W=16, ctx_lo=0, ctx_hi=200, masks="mixed"),
+    W_("com_full_accept", B=4, Hq=4, Hkv=4, D=64, W=20, ctx_lo=5, ctx_hi=40, match_p=1.0),
+    W_("com_fp32", B=3, Hq=4, Hkv=2, W=9, dtype="f32", ctx_lo=14, ctx_hi=18, masks="tree"),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("skip_root", [False, True])
+@pytest.mark.parametrize("wl", COMMIT, ids=[w.name for w in COMMIT])
+def test_commit_bit_exact(wl, skip_root, fused):
+    inp = gpu_inputs(wl, 5)
+    n_ref, path_ref, bonus_ref = oracle_accept(inp)
+    kc0, vc0 = raw(inp["k_cache"]), raw(inp["v_cache"])
+    kc_ref, vc_ref, ctx_ref = O.kv_commit(kc0, vc0, raw(inp["k_new"]), raw(inp["v_new"]), n_ref,
+                                          path_ref, ints(inp["block_table"]),
+                                          ints(inp["ctx_lens"]), skip_root)
+    ctx_out = torch.full_like(inp["ctx_lens"], -7)
+    if fused:
+        n, path, bonus, ctx_out = lib.accept_commit(
+            inp["logits"], inp["draft_ids"], inp["mask_kind"], inp["mask_ids"], inp["k_new"],
+            inp["v_new"], inp["block_table"], inp["ctx_lens"], inp["k_cache"], inp["v_cache"],
+            ctx_lens_out=ctx_out, skip_root=skip_root)
+        assert_accept_equal((n, path, bonus), (n_ref, path_ref, bonus_ref))
+    else:
+        n = torch.from_numpy(n_ref.astype(np.int32)).cuda()
+        path = torch.from_numpy(path_ref.astype(np.int32)).cuda()
+        lib.kv_commit(inp["k_new"], inp["v_new"], n, path, inp["block_table"], inp["ctx_lens"],
+                      inp["k_cache"], inp["v_cache"], ctx_lens_out=ctx_out, skip_root=skip_root)
+    torch.cuda.synchronize()
+    assert np.array_equal(ints(ctx_out), ctx_ref)
+    assert np.array_equal(raw(inp["k_cache"]), kc_ref)
+    assert np.array_equal(raw(inp["v_cache"]), vc_ref)
+
+
+def test_commit_in_place_context_update_and_idempotence():
+    wl = W_("com_inplace", B=5, Hq=8, Hkv=2, W=8, ctx_lo=3, ctx_hi=100, masks="mixed")
+    inp = gpu_inputs(wl, 9)
+    n_ref, path_ref, _ = oracle_accept(inp)
+    ctx0 = inp["ctx_lens"].clone()
+    kc_ref, vc_ref, ctx_ref = O.kv_commit(raw(inp["k_cache"]), raw(inp["v_cache"]),
+                                          raw(inp["k_new"]), raw(inp["v_new"]), n_ref, path_ref,
+                                          ints(inp["block_table"]), ints(ctx0))
+    # the same commit twice from the same boundary, then once in place
+    for _ in range(2):
+        out = lib.accept_commit(inp["logits"], inp["draft_ids"], inp["mask_kind"],
+                                inp["mask_ids"], inp["k_new"], inp["v_new"], inp["block_table"],
+                                ctx0, inp["k_cache"], inp["v_cache"])[3]
+    ctx = ctx0.clone()
+    lib.accept_commit(inp["logits"], inp["draft_ids"], inp["mask_kind"], inp["mask_ids"],
+                      inp["k_new"], inp["v_new"], inp["block_table"], ctx, inp["k_cache"],
+                      inp["v_cache"], ctx_lens_out=ctx)
+    torch.cuda.synchronize()
+    assert np.array_equal(ints(out), ctx_ref) and np.array_equal(ints(ctx), ctx_ref)
+    assert np.array_equal(raw(inp["k_cache"]), kc_ref)
+    assert np.array_equal(raw(inp["v_cache"]), vc_ref)
+
+
+def test_commit_then_attend_equals_verify_rows():
+    """After committing an accepted chain, decoding accepted row i as a
+    one-row block at context L+i reproduces row i of the verify output."""
+    wl = W_("com_decode", B=2, Hq=8, Hkv=2, W=6, ctx_lo=20, ctx_hi=60, match_p=1.0)
+    inp = gpu_inputs(wl, 12)
+    out, _ = run_attn(inp)
+    lib.accept_commit(inp["logits"], inp["draft_ids"], inp["mask_kind"], inp["mask_ids"],
+                      inp["k_new"], inp["v_new"], inp["block_table"], inp["ctx_lens"],
+                      inp["k_cache"], inp["v_cache"])
+    for i in range(wl.W):
+        ctx_i = inp["ctx_lens"] + i
+        o1, _ = lib.verify_attn(inp["q"][:, i:i + 1].contiguous(), inp["k_cache"], inp["v_cache"],
+                                inp["block_table"], ctx_i, inp["k_new"][:, i:i + 1].contiguous(),
+                                inp["v_new"][:, i:i + 1].contiguous(),
+                                torch.zeros_like(inp["mask_kind"]),
+                                torch.full((wl.B, 1), -1, dtype=torch.int32, device="cuda"),
+                                max_ctx_len=int(ints(ctx_i).max()), scale=inp["scale"])
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(o1[:, 0].cpu().numpy(), out[:, i].cpu().numpy(),
+                                   atol=2e-3, rtol=2e-2)
+
+
+# ----------------------------------------------------------------------------
+# data errors: poisoned outputs and the sticky status word, never a fault
+# ----------------------------------------------------------------------------
+
+def test_malformed_mask_poisons_only_that_sequence():
+    wl = W_("bad_mask", B=3, Hq=8, Hkv=2, W=8, ctx_lo=30, ctx_hi=90, masks="tree")
+    inp = gpu_inputs(wl, 2)
+    lib.device_status(clear=True)
+    ids = inp["mask_ids"].clone()
+    ids[1, 5] = 6  # a parent after its child
+    inp["mask_ids"] = ids
+    out, lse = run_attn(inp)
+    assert torch.isnan(out[1]).all() and torch.isnan(lse[1]).all()
+    ref_out, ref_lse = oracle_attn(inp)
+    keep = torch.tensor([0, 2], device=out.device)
+    assert_attn_close(out[keep], lse[keep], ref_out[[0, 2]], ref_lse[[0, 2]], *tol_for(wl))
+    n, path, bonus = lib.accept(inp["logits"], inp["draft_ids"], inp["mask_kind"], ids)
+    assert_accept_equal((n, path, bonus), oracle_accept(inp))
+    assert lib.device_status(clear=True) & lib.DEV_BAD_MASK
+
+
+def test_context_above_bound_poisons_that_sequence():
+    wl = W_("bad_ctx", B=2, Hq=8, Hkv=2, W=4, ctx_lo=40, ctx_hi=40)
+    inp = gpu_inputs(wl, 2)
+    lib.device_status(clear=True)
+    out, lse = run_attn(inp, max_ctx_len=39)
+    assert torch.isnan(out).all() and torch.isnan(lse).all()
+    assert lib.device_status(clear=True) & lib.DEV_BAD_CTX
+
+
+def test_unmapped_committed_page_poisons_the_rows_that_read_it():
+    wl = W_("bad_page", B=2, Hq=8, Hkv=2, W=4, ctx_lo=100, ctx_hi=100)
+    inp = gpu_inputs(wl, 2)
+    lib.device_status(clear=True)
+    bt = inp["block_table"].clone()
+    bt[0, 2] = inp["k_cache"].shape[0] + 5
+    inp["block_table"] = bt
+    out, lse = run_attn(inp)
+    assert torch.isnan(out[0]).all()
+    assert torch.isfinite(out[1]).all()
+    assert lib.device_status(clear=True) & lib.DEV_BAD_PAGE
+
+
+def test_commit_with_unmapped_target_slot_writes_nothing():
+    wl = W_("bad_commit", B=3, Hq=4, Hkv=2, W=8, ctx_lo=30, ctx_hi=30, match_p=1.0)
+    inp = gpu_inputs(wl, 2)
+    lib.device_status(clear=True)
+    bt = inp["block_table"].clone()
+    bt[1, (30 + 7) // 16] = -1
+    kc0, vc0 = raw(inp["k_cache"]), raw(inp["v_cache"])
+    n_ref, path_ref, _ = oracle_accept(inp)
+    kc_ref, vc_ref, ctx_ref = O.kv_commit(kc0, vc0, raw(inp["k_new"]), raw(inp["v_new"]), n_ref,
+                                          path_ref, ints(bt), ints(inp["ctx_lens"]))
+    _, _, _, ctx = lib.accept_commit(inp["logits"], inp["draft_ids"], inp["mask_kind"],
+                                     inp["mask_ids"], inp["k_new"], inp["v_new"], bt,
+                                     inp["ctx_lens"], inp["k_cache"], inp["v_cache"])
+    torch.cuda.synchronize()
+    assert np.array_equal(ints(ctx), ctx_ref) and ctx_ref[1] == 30
+    assert np.array_equal(raw(inp["k_cache"]), kc_ref)
+    assert np.array_equal(raw(inp["v_cache"]), vc_ref)
+    assert lib.device_status(clear=True) & lib.DEV_BAD_PAGE
+
+
+def test_empty_batch_is_a_no_op():
+    wl = W_("empty", B=1, Hq=4, Hkv=2, W=4, ctx_lo=10, ctx_hi=10)
+    inp = gpu_inputs(wl, 1)
+    e = lambda t: t[:0]
+    out, lse = lib.verify_attn(e(inp["q"]), inp["k_cache"], inp["v_cache"], e(inp["block_table"]),
+                               e(inp["ctx_lens"]), e(inp["k_new"]), e(inp["v_new"]),
+                               e(inp["mask_kind"]), e(inp["mask_ids"]), max_ctx_len=10)
+    torch.cuda.synchronize()
+    assert out.numel() == 0
