@@ -111,15 +111,15 @@ __device__ inline int wave_accept(const AcceptParams& p, int b, const int* s_tgt
   const int best = 63 - (key & 63);
   const int len = key >> 6;
   const uint64_t ab = shfl64(anc, best);
-  if (in) {
-    if ((ab >> lane) & 1ull) {
-      const int pos = __popcll(ab & ((1ull << lane) - 1ull));
-      path[pos] = lane;
-      s_path[pos] = lane;
-    } else if (lane > len) {
-      path[lane] = -1;
-    }
+  // Path nodes write themselves to their depth; positions past the accepted
+  // length are padded by the lane of the same index (a different address
+  // even when that lane is itself a path node: its depth is <= len < lane).
+  if (in && ((ab >> lane) & 1ull)) {
+    const int pos = __popcll(ab & ((1ull << lane) - 1ull));
+    path[pos] = lane;
+    s_path[pos] = lane;
   }
+  if (in && lane > len) path[lane] = -1;
   if (lane == 0) {
     p.accept_len[b] = len;
     p.bonus_id[b] = s_tgt[best];

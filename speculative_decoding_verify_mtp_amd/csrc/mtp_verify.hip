@@ -63,8 +63,10 @@ Plan make_plan(const mtp_shape& s) {
   pl.R = s.W * pl.g;
   pl.mfma = s.dtype == MTP_BF16 && pl.R >= 16;
   if (pl.mfma) {
+    // Row tiles per wave: 1, 2 or 4 (a third tile is padded to four so the
+    // K/V stream is still read once).
     const int tiles = (pl.R + 15) / 16;
-    pl.RB = tiles >= 4 ? 4 : tiles;
+    pl.RB = tiles >= 3 ? 4 : tiles;
     pl.nRB = (tiles + pl.RB - 1) / pl.RB;
   } else {
     pl.RB = 0;

@@ -103,14 +103,14 @@ def test_empty_batch_needs_no_pointers(L):
 
 def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     """The documented split plan: rows per KV head R = W * g; bf16 with R >= 16
-    runs on MFMA in row blocks of up to 64 rows, everything else in chunks of
+    runs on MFMA in row blocks of 16, 32 or 64 rows, everything else in chunks of
     4 rows; the automatic split is the power of two giving about 2048 work
     items, clamped to [64, 2048] tokens."""
     g = Hq // Hkv
     R = W * g
     if dtype == lib.MTP_BF16 and R >= 16:
         tiles = (R + 15) // 16
-        rb = min(4, tiles)
+        rb = 4 if tiles >= 3 else tiles
         nrb = (tiles + rb - 1) // rb
     else:
         nrb = (R + 3) // 4
