@@ -118,6 +118,11 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=0, help="KV pool replicas (0 = auto, >= 1 GB)")
     ap.add_argument("--warm", action="store_true", help="one replica (cache-warm numbers)")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--linear-pages", action="store_true",
+                    help="identity page order instead of the shuffled pool (comparison only)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only time a plain device copy of MB megabytes (HBM reference and "
+                         "the FETCH_SIZE/WRITE_SIZE calibration kernel), then exit")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -133,7 +138,28 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.copy_calibration:
+        n = args.copy_calibration * 1000 * 1000
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        a.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        z.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(z) / reps
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                          "read_plus_write_GBs": 2 * n / ms / 1e6}), flush=True)
+        return 0
+
     wl = I.WORKLOADS[args.workload]
+    if args.linear_pages:
+        wl = wl.scaled(shuffle_pages=False)
     if args.seg_lookback is not None:
         wl = wl.scaled(seg_lookback=args.seg_lookback)
     seed = I.workload_seed(args.workload)

@@ -45,19 +45,63 @@ struct CommitParams {
   int row_bytes;  // Hkv * D * element size, a multiple of 16
 };
 
-// Argmax of every block row into s_tgt[0..W).  All 256 threads take part.
+// Inputs of wave 0 loaded before the argmax, so that their latency overlaps
+// the logits stream: this lane's mask id and draft id, the mask kind, and for
+// the commit the context length and the page of slot ctx + lane.
+struct Prefetch {
+  int kind, id, draft, L, page;
+};
+
+__device__ inline Prefetch prefetch_inputs(const AcceptParams& ap, const CommitParams* cp, int b) {
+  const int lane = threadIdx.x & 63;
+  const int W = ap.W;
+  Prefetch f;
+  f.kind = ap.mask_kind[b];
+  f.id = lane < W ? ap.mask_ids[(size_t)b * W + lane] : 0;
+  f.draft = lane < W ? ap.draft_ids[(size_t)b * W + lane] : -1;
+  f.L = 0;
+  f.page = -1;
+  if (cp != nullptr) {
+    f.L = cp->ctx_in[b];
+    const int t = f.L + lane;
+    const int pi = t >> 4;
+    if (lane < W && f.L >= 0 && pi < cp->max_pages) f.page = cp->block_table[(size_t)b * cp->max_pages + pi];
+  }
+  return f;
+}
+
+// Argmax of every block row into s_tgt[0..W).  All 256 threads take part;
+// 16-byte loads when rows are 16-byte aligned (V % 4 == 0).
 __device__ inline void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  const bool vec = (p.V & 3) == 0 && ((uintptr_t)p.logits & 15) == 0;
   for (int i = wv; i < p.W; i += 4) {
     const float* row = p.logits + ((size_t)b * p.W + i) * p.V;
     float bv = neg_inf();
     int bi = 0x7fffffff;
-    for (int v = lane; v < p.V; v += kWave) {
-      const float x = row[v];
-      if (x > bv || bi == 0x7fffffff) {
-        bv = x;
-        bi = v;
+    if (vec) {
+      const float4* r4 = reinterpret_cast<const float4*>(row);
+      const int n4 = p.V >> 2;
+#pragma unroll 4
+      for (int v = lane; v < n4; v += kWave) {
+        const float4 x = r4[v];
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (xs[e] > bv || bi == 0x7fffffff) {
+            bv = xs[e];
+            bi = 4 * v + e;
+          }
+        }
+      }
+    } else {
+      for (int v = lane; v < p.V; v += kWave) {
+        const float x = row[v];
+        if (x > bv || bi == 0x7fffffff) {
+          bv = x;
+          bi = v;
+        }
       }
     }
 #pragma unroll
@@ -75,20 +119,19 @@ __device__ inline void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
 
 // Acceptance of sequence b by wave 0 (lane = node).  Returns the accepted
 // length (-1 for a malformed mask) and fills s_path[0..len] with the path.
-__device__ inline int wave_accept(const AcceptParams& p, int b, const int* s_tgt, int* s_path) {
+__device__ inline int wave_accept(const AcceptParams& p, int b, const Prefetch& f, const int* s_tgt,
+                                  int* s_path) {
   const int lane = threadIdx.x & 63;
   const int W = p.W;
   const bool in = lane < W;
-  const int kind = p.mask_kind[b];
-  const int32_t* ids = p.mask_ids + (size_t)b * W;
   bool ok;
   uint64_t anc;
   int par;
-  if (kind == MTP_MASK_TREE) {
-    anc = node_visibility(kind, ids, W, -1, lane, ok);
-    par = (in && lane >= 1 && ok) ? ids[lane] : 0;
+  if (f.kind == MTP_MASK_TREE) {
+    anc = node_visibility(f.kind, f.id, W, -1, lane, ok);
+    par = (in && lane >= 1 && ok) ? f.id : 0;
   } else {
-    node_visibility(kind, ids, W, -1, lane, ok);  // validates the description
+    node_visibility(f.kind, f.id, W, -1, lane, ok);  // validates the description
     anc = in ? (~0ull >> (63 - lane)) : 0ull;
     par = lane >= 1 ? lane - 1 : 0;
   }
@@ -102,8 +145,7 @@ __device__ inline int wave_accept(const AcceptParams& p, int b, const int* s_tgt
     }
     return -1;
   }
-  const int d = in ? p.draft_ids[(size_t)b * W + lane] : -1;
-  const bool match = in && lane >= 1 && d >= 0 && d == s_tgt[par];
+  const bool match = in && lane >= 1 && f.draft >= 0 && f.draft == s_tgt[par];
   const uint64_t mm = __ballot(match) | 1ull;
   const bool acc = in && (anc & ~mm) == 0ull;
   const int depth = __popcll(anc) - 1;
@@ -127,33 +169,32 @@ __device__ inline int wave_accept(const AcceptParams& p, int b, const int* s_tgt
   return len;
 }
 
-// Commit of sequence b.  `a` (accepted length) and s_path are valid in wave 0
-// when fused; otherwise pass fused = false and they are read from memory.
+// Commit of sequence b.  Wave 0 validates (one path position per lane) and
+// publishes the copy list in LDS; then all threads copy.  When fused, `a` and
+// s_path come from the acceptance; otherwise they are read from memory.
 template <bool kFused>
-__device__ inline void block_commit(const CommitParams& p, int b, int a_fused, const int* s_path,
-                                    int* s_src, int* s_dst, int* s_meta) {
+__device__ inline void block_commit(const CommitParams& p, int b, const Prefetch& f, int a_fused,
+                                    const int* s_path, int* s_src, int* s_dst, int* s_meta) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < kWave) {
     const int a = kFused ? a_fused : p.accept_len[b];
-    const int L = p.ctx_in[b];
+    const int L = f.L;
     const int first = p.skip_root ? 1 : 0;
     const bool a_ok = a >= 0 && a <= p.W - 1 && L >= 0;
     bool bad_k = false;
     if (a_ok && lane >= first && lane <= a) {
       const int row = kFused ? s_path[lane] : p.accept_path[(size_t)b * p.W + lane];
-      const int t = L + lane;
-      const int pi = t >> 4;
-      const int pg = pi < p.max_pages ? p.block_table[(size_t)b * p.max_pages + pi] : -1;
+      const int pg = f.page;
       bad_k = row < 0 || row >= p.W || pg < 0 || pg >= p.num_pages;
       s_src[lane] = row;
-      s_dst[lane] = pg * kPage + (t & 15);
+      s_dst[lane] = pg * kPage + ((L + lane) & 15);
     }
     const bool bad = __ballot(bad_k) != 0ull;
     if (lane == 0) {
       const bool good = a_ok && !bad;
       s_meta[0] = good ? a : -1;
       s_meta[1] = first;
-      p.ctx_out[b] = good ? L + a + 1 : L;  // L was read above by this lane
+      p.ctx_out[b] = good ? L + a + 1 : L;  // L was read before any write of ctx_out
       if (!good) raise_status(a_ok ? MTP_DEV_BAD_PAGE : MTP_DEV_BAD_ACCEPT);
     }
   }
@@ -181,16 +222,28 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptParams p) {
   __shared__ int s_tgt[MTP_MAX_W];
   __shared__ int s_path[MTP_MAX_W];
   const int b = blockIdx.x;
+  Prefetch f{};
+  if (threadIdx.x < kWave) f = prefetch_inputs(p, nullptr, b);
   block_argmax(p, b, s_tgt);
   __syncthreads();
-  if (threadIdx.x < kWave) wave_accept(p, b, s_tgt, s_path);
+  if (threadIdx.x < kWave) wave_accept(p, b, f, s_tgt, s_path);
 }
 
 __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
   __shared__ int s_src[MTP_MAX_W];
   __shared__ int s_dst[MTP_MAX_W];
   __shared__ int s_meta[2];
-  block_commit<false>(p, blockIdx.x, 0, nullptr, s_src, s_dst, s_meta);
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  Prefetch f{};
+  f.page = -1;
+  if (threadIdx.x < kWave) {  // only wave 0 reads ctx_in (ctx_out may alias it)
+    f.L = p.ctx_in[b];
+    const int pi = (f.L + lane) >> 4;
+    if (lane < p.W && f.L >= 0 && pi < p.max_pages)
+      f.page = p.block_table[(size_t)b * p.max_pages + pi];
+  }
+  block_commit<false>(p, b, f, 0, nullptr, s_src, s_dst, s_meta);
 }
 
 __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptParams ap, CommitParams cp) {
@@ -200,12 +253,14 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptParams ap, Com
   __shared__ int s_dst[MTP_MAX_W];
   __shared__ int s_meta[2];
   const int b = blockIdx.x;
+  Prefetch f{};
+  if (threadIdx.x < kWave) f = prefetch_inputs(ap, &cp, b);
   block_argmax(ap, b, s_tgt);
   __syncthreads();
   int a = -1;
-  if (threadIdx.x < kWave) a = wave_accept(ap, b, s_tgt, s_path);
+  if (threadIdx.x < kWave) a = wave_accept(ap, b, f, s_tgt, s_path);
   __syncthreads();
-  block_commit<true>(cp, b, a, s_path, s_src, s_dst, s_meta);
+  block_commit<true>(cp, b, f, a, s_path, s_src, s_dst, s_meta);
 }
 
 }  // namespace mtpv

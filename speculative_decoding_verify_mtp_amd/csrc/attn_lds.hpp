@@ -1,0 +1,332 @@
+// Split-K verify attention, D = 128, bf16 MFMA, K/V streamed through an LDS
+// ring by direct-to-LDS loads (global_load_lds_dwordx4).
+//
+// One workgroup = one work item (sequence, KV head, row block, split).  Its
+// NR waves (1, 2 or 4) split the rows: wave w owns RB row tiles of 16 rows.
+// All waves consume the same K/V, so the committed context is read from HBM
+// once per row block and shared through LDS.
+//
+// A stage is 32 keys (two pages) = 16 KB, stored as sixteen 1 KB "register
+// images": image i holds, at byte 16 * lane, exactly the 16 bytes that lane
+// needs as an MFMA operand (the layouts of attn_mfma.hpp):
+//   images 0..7  : K operand of 16-key half kt = i / 4, d-chunk m = i % 4:
+//                  lane (c, q) <- K[key 16 kt + c][32 m + 8 q .. +8)
+//   images 8..15 : V vectors e = i - 8: lane (c, q) <- V[pv_key(q, e)][8 c .. +8)
+// The direct-to-LDS load writes lane l's 16 bytes to M0 + 16 l, so a stage is
+// sixteen such loads (16 / NR per wave) and every later LDS read is one
+// conflict-free 16-byte read per lane.
+//
+// The ring holds kStages stages; kStages - 1 are in flight while one is being
+// computed.  Each wave waits for its own loads of stage s (s_waitcnt vmcnt
+// with an explicit count), then a workgroup barrier makes everybody's loads
+// visible and also proves that stage s - 1 is no longer read, so its slot
+// takes stage s + kStages - 1.  The loads are issued through inline assembly:
+// the compiler would otherwise guard every LDS read with a full vmcnt(0) wait
+// and serialise the pipeline.
+#pragma once
+
+#include "attn_mfma.hpp"
+#include "common.hpp"
+
+namespace mtpv {
+
+constexpr int kLdsStages = 5;  // 80 KB per workgroup: two workgroups fill gfx950's 160 KB
+constexpr int kStageBytes = 16 * 1024;
+constexpr int kMaxSplitPages = 128;  // page indices of a split held in two registers per lane
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// 16 bytes from global `g` into LDS at m0 + 16 * lane, m0 = lds (wave-uniform).
+// m0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(base)
+      : "memory");
+}
+
+// Same, addressed as a wave-uniform 64-bit base (SGPRs) plus a per-lane 32-bit
+// byte offset: the form used for whole stages, whose per-lane offsets are
+// fixed for the whole item.
+__device__ __forceinline__ void dma16_sbase(uint32_t voff, uint64_t sbase, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sbase);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(m0v)
+      : "memory");
+}
+
+// Waits until at most N vector-memory operations of this wave are
+// outstanding, then joins the workgroup barrier.  One asm statement with a
+// memory clobber, so no LDS read can be scheduled above the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmem_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Wait for this wave's loads of a stage when n later stages (PER loads each)
+// may stay in flight, then barrier.
+template <int PER>
+__device__ __forceinline__ void wait_stage_barrier(int n) {
+  static_assert(kLdsStages <= 5, "wait counts below cover up to three later stages");
+  if (n <= 0)
+    wait_vmem_barrier<0>();
+  else if (n == 1)
+    wait_vmem_barrier<PER>();
+  else if (n == 2)
+    wait_vmem_barrier<2 * PER>();
+  else
+    wait_vmem_barrier<3 * PER>();
+}
+
+// RB = 1 kernels are held to 256 registers so that two waves share a SIMD.
+template <int RB, int NR>
+__global__ __launch_bounds__(64 * NR) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
+void attn_partial_lds(AttnParams p) {
+  constexpr int D = 128;
+  constexpr int NC = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int IPW = 16 / NR;  // images per wave per stage
+  __shared__ __attribute__((aligned(16))) char ring[kLdsStages * kStageBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int c = lane & 15;
+  const int qd = lane >> 4;
+  const int b = blockIdx.y;
+  const Item it = decode_item(blockIdx.x, p);
+  if (it.split >= p.max_splits) return;  // uniform over the workgroup
+  const int L = p.ctx_lens[b];
+  if (L < 0 || L > p.max_ctx) return;
+  const int ns = num_splits(L, p.S);
+  if (it.split >= ns) return;
+  const int start = it.split * p.S;
+  const int end = min(L, start + p.S);
+  const bool last = it.split == ns - 1;
+
+  const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache) + (size_t)it.kvh * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache) + (size_t)it.kvh * D;
+  const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (size_t)it.kvh * D;
+  const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (size_t)it.kvh * D;
+  const size_t slot_stride = (size_t)p.Hkv * D;
+
+  // ---- set-up loads: page indices of the split, Q operands, in-block mask
+  const int npg = (end - start + kPage - 1) / kPage;
+  const int32_t* btrow = p.block_table + (size_t)b * p.max_pages + start / kPage;
+  int pr0 = lane < npg ? btrow[lane] : 0;
+  int pr1 = lane + 64 < npg ? btrow[lane + 64] : 0;
+  bool bad = (lane < npg && (unsigned)pr0 >= (unsigned)p.num_pages) ||
+             (lane + 64 < npg && (unsigned)pr1 >= (unsigned)p.num_pages);
+  bad = __ballot(bad) != 0ull;
+  if ((unsigned)pr0 >= (unsigned)p.num_pages) pr0 = 0;
+  if ((unsigned)pr1 >= (unsigned)p.num_pages) pr1 = 0;
+
+  const int row_tile0 = (it.rb * NR + wv) * RB;
+  bf16x8 qf[RB][NC];
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    const int rho = (row_tile0 + k) * 16 + c;
+    if (rho < p.R) {
+      const int w = rho / p.g;
+      const int j = rho - w * p.g;
+      const uint16_t* src = static_cast<const uint16_t*>(p.q) +
+                            ((size_t)(b * p.W + w) * p.Hq + (size_t)it.kvh * p.g + j) * D + qd * 8;
+#pragma unroll
+      for (int m = 0; m < NC; ++m) qf[k][m] = load_bf16x8(src + m * 32);
+    } else {
+#pragma unroll
+      for (int m = 0; m < NC; ++m) qf[k][m] = bf16x8{};
+    }
+  }
+
+  int ntail = 0;
+  uint64_t vrow[RB];
+#pragma unroll
+  for (int k = 0; k < RB; ++k) vrow[k] = 0;
+  if (last) {
+    bool ok;
+    const uint64_t vnode =
+        node_visibility(p.mask_kind[b], lane_mask_id(p, b, lane), p.W, p.lookback, lane, ok);
+    if (ok) {
+      ntail = (p.W + 31) / 32;
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        const int rho = min((row_tile0 + k) * 16 + c, p.R - 1);
+        vrow[k] = shfl64(vnode, rho / p.g);
+      }
+    }
+  }
+  const int ncs = (end - start + 31) / 32;  // committed stages
+  const int nst = ncs + ntail;
+  // The set-up loads are complete before the first stage is issued (a wait the
+  // compiler sees, so it adds none of its own inside the pipeline).
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- stage issue: this wave's images of stage s into ring slot s % kStages
+  // Per-lane byte offsets inside a page for whole stages: a K image (kt, m)
+  // is koff + 64 m, a V image e is voff + (e & 3) * slot_bytes; the page (p0 or
+  // p1) goes into the wave-uniform base.
+  const uint32_t ring_base = lds_offset(ring);
+  const uint32_t slot_bytes = (uint32_t)(slot_stride * 2);
+  const uint64_t page_bytes = (uint64_t)kPage * slot_bytes;
+  const uint32_t koff = (uint32_t)c * slot_bytes + 16u * qd;
+  const uint32_t voff = 4u * qd * slot_bytes + 16u * c;
+  const uint64_t kc_addr = (uint64_t)(uintptr_t)kc, vc_addr = (uint64_t)(uintptr_t)vc;
+  auto issue = [&](int s) {
+    const uint32_t slot_base = ring_base + (uint32_t)(s % kLdsStages) * kStageBytes;
+    if (s < ncs) {
+      const int t0 = start + 32 * s;
+      const int nk = end - t0;
+      const int rp = 2 * s;  // page of the split holding key 0 of the stage
+      const int p0 = __builtin_amdgcn_readlane(rp < 64 ? pr0 : pr1, rp & 63);
+      const int p1 = nk > 16 ? __builtin_amdgcn_readlane(rp + 1 < 64 ? pr0 : pr1, (rp + 1) & 63) : p0;
+      if (nk >= 32) {
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) {
+          const int im = wv + NR * k;
+          const bool second = im < 8 ? (im >> 2) != 0 : (im - 8) >= 4;
+          const uint64_t base = (im < 8 ? kc_addr : vc_addr) + (uint64_t)(second ? p1 : p0) * page_bytes;
+          const uint32_t off = im < 8 ? koff + 64u * (im & 3) : voff + ((im - 8) & 3) * slot_bytes;
+          dma16_sbase(off, base, slot_base + (uint32_t)im * 1024u);
+        }
+        return;
+      }
+#pragma nounroll
+      for (int im = wv; im < 16; im += NR) {
+        const uint16_t* src;
+        if (im < 8) {
+          const int kt = im >> 2, m = im & 3;
+          const int key = 16 * kt + c;
+          const bool v = key < nk;
+          const int pg = v ? (kt ? p1 : p0) : p0;
+          src = kc + ((size_t)pg * kPage + (v ? c : 0)) * slot_stride + 32 * m + 8 * qd;
+        } else {
+          const int e = im - 8;
+          const int key = pv_key(qd, e);
+          const bool v = key < nk;
+          const int pg = v ? (e < 4 ? p0 : p1) : p0;
+          src = vc + ((size_t)pg * kPage + (v ? (key & 15) : 0)) * slot_stride + 8 * c;
+        }
+        dma16(src, slot_base + (uint32_t)im * 1024u);
+      }
+    } else {
+      const int j0 = 32 * (s - ncs);
+#pragma nounroll
+      for (int im = wv; im < 16; im += NR) {
+        const uint16_t* src;
+        if (im < 8) {
+          const int kt = im >> 2, m = im & 3;
+          int j = j0 + 16 * kt + c;
+          j = j < p.W ? j : 0;
+          src = kn + (size_t)(b * p.W + j) * slot_stride + 32 * m + 8 * qd;
+        } else {
+          int j = j0 + pv_key(qd, im - 8);
+          j = j < p.W ? j : 0;
+          src = vn + (size_t)(b * p.W + j) * slot_stride + 8 * c;
+        }
+        dma16(src, slot_base + (uint32_t)im * 1024u);
+      }
+    }
+  };
+
+  MfmaState<D, RB> st;
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    st.m[k] = neg_inf();
+    st.l[k] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int s = 0; s < kLdsStages - 1 && s < nst; ++s) issue(s);
+
+  for (int s = 0; s < nst; ++s) {
+    const int after = min(kLdsStages - 2, nst - 1 - s);
+    wait_stage_barrier<IPW>(after);
+    if (s + kLdsStages - 1 < nst) issue(s + kLdsStages - 1);
+
+    const char* buf = ring + (s % kLdsStages) * kStageBytes + lane * 16;
+    bf16x8 kf[2][NC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int m = 0; m < NC; ++m)
+        kf[kt][m] = *reinterpret_cast<const bf16x8*>(buf + (kt * 4 + m) * 1024);
+    VRow<D> vv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vv[e].v = *reinterpret_cast<const uint4*>(buf + (8 + e) * 1024);
+
+    if (s < ncs) {
+      const int nk = end - (start + 32 * s);
+      if (nk >= 32) {
+        mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [](int, int) { return true; });
+      } else {
+        mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st,
+                         [&](int, int e) { return pv_key(qd, e) < nk; });
+      }
+    } else {
+      const int j0 = 32 * (s - ncs);
+      mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [&](int k, int e) {
+        return ((vrow[k] >> (j0 + pv_key(qd, e))) & 1ull) != 0ull;
+      });
+    }
+  }
+
+  if (bad) {
+    if (threadIdx.x == 0) raise_status(MTP_DEV_BAD_PAGE);
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      st.m[k] = qnan();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{qnan(), qnan(), qnan(), qnan()};
+    }
+  }
+
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    float l = st.l[k];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int rho = (row_tile0 + k) * 16 + c;
+    if (rho < p.R) {
+      const size_t pidx =
+          (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R + rho;
+      if (qd == 0) {
+        p.part_ml[2 * pidx] = st.m[k];
+        p.part_ml[2 * pidx + 1] = l;
+      }
+      float* dst = p.part_acc + pidx * D + qd * (D / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int t = 0; t < NT; t += 4) {
+          float4 v;
+          v.x = st.acc[k][t][e];
+          v.y = st.acc[k][t + 1][e];
+          v.z = st.acc[k][t + 2][e];
+          v.w = st.acc[k][t + 3][e];
+          *reinterpret_cast<float4*>(dst + e * (D / 16) + t) = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace mtpv

@@ -64,15 +64,18 @@ __device__ __forceinline__ unsigned vrow_dword(const VRow<D>& r, int i) {
 }
 
 // Operand A of the PV product for output column tile t: element t of each of
-// the lane's 8 V vectors, packed pairwise.
+// the lane's 8 V vectors, packed pairwise with one byte permute per dword
+// (v_perm_b32: selector bytes 0-3 pick from the second source, 4-7 from the
+// first).
 template <int D, int T>
 __device__ __forceinline__ bf16x8 pack_v_operand(const VRow<D> (&vv)[8]) {
+  constexpr unsigned kSel = (T & 1) ? 0x07060302u : 0x05040100u;
   unsigned w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const unsigned x = vrow_dword<D>(vv[2 * j], T >> 1);
     const unsigned y = vrow_dword<D>(vv[2 * j + 1], T >> 1);
-    w[j] = (T & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+    w[j] = __builtin_amdgcn_perm(y, x, kSel);  // (x, y) halves T&1 -> low, high
   }
   bf16x8 r;
   __builtin_memcpy(&r, w, sizeof(r));
@@ -85,10 +88,16 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 
 template <int D, int RB>
 struct MfmaState {
-  float m[RB];           // running row max (log2 domain), replicated over the 4 quarters
+  float m[RB];           // reference row max (log2 domain), replicated over the 4 quarters
   float l[RB];           // this lane's share of the running row sum
   f32x4 acc[RB][D / 16];  // acc^T tiles
 };
+
+// The reference max of a row only moves when the row max exceeds it by more
+// than this many log2 units, so the accumulator rescale (a read-modify-write
+// of every accumulator register) is skipped on almost every tile.  Weights
+// relative to the reference stay below 2^8, far from fp32 overflow.
+constexpr float kRescaleSlack = 8.f;
 
 // One 32-key tile: scores, online-softmax update, PV accumulate.
 // kf: K operands of the two 16-key halves; vv: V vectors of keys
@@ -113,36 +122,41 @@ __device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][m], qf[k][m], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][m], qf[k][m], s1, 0, 0, 0);
     }
+    // raw scores; the scale (> 0) is applied after the max and inside the exp
     float x[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[e] = s0[e] * scale_log2;
-      x[4 + e] = s1[e] * scale_log2;
+      x[e] = s0[e];
+      x[4 + e] = s1[e];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (!vis(k, e)) x[e] = neg_inf();
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(st.m[k], mx);
-    const float muse = mnew == neg_inf() ? 0.f : mnew;
-    const float alpha = fast_exp2(st.m[k] - muse);
+    mx *= scale_log2;
+    const float mold = st.m[k];
+    const float mref = mx > mold + kRescaleSlack ? mx : mold;
+    const float muse = mref == neg_inf() ? 0.f : mref;
     float sum = 0.f;
     __bf16 ph[8], plo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(x[e] - muse);
+      const float pe = fast_exp2(fmaf(x[e], scale_log2, -muse));
       sum += pe;
       ph[e] = (__bf16)pe;
       plo[e] = (__bf16)(pe - (float)ph[e]);
     }
-    st.l[k] = st.l[k] * alpha + sum;
-    st.m[k] = mnew;
+    if (__ballot(mref != mold) != 0ull) {  // wave-uniform: rare after the first tile
+      const float alpha = fast_exp2(mold - muse);
+      st.l[k] *= alpha;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) st.acc[k][t] *= alpha;
+      for (int t = 0; t < NT; ++t) st.acc[k][t] *= alpha;
+    }
+    st.l[k] += sum;
+    st.m[k] = mref;
     __builtin_memcpy(&pf[k], ph, sizeof(bf16x8));
     __builtin_memcpy(&pl[k], plo, sizeof(bf16x8));
   }
@@ -270,7 +284,7 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
   if (last) {
     bool ok;
     const uint64_t vnode =
-        node_visibility(p.mask_kind[b], p.mask_ids + (size_t)b * p.W, p.W, p.lookback, lane, ok);
+        node_visibility(p.mask_kind[b], lane_mask_id(p, b, lane), p.W, p.lookback, lane, ok);
     if (ok) {
       uint64_t vrow[RB];
 #pragma unroll

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
   if (last) {
     bool ok;
     const uint64_t vnode =
-        node_visibility(p.mask_kind[b], p.mask_ids + (size_t)b * p.W, p.W, p.lookback, lane, ok);
+        node_visibility(p.mask_kind[b], lane_mask_id(p, b, lane), p.W, p.lookback, lane, ok);
     if (ok) {
       ntail = p.W;
 #pragma unroll

@@ -65,14 +65,15 @@ __device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
 //            pointer jumping, 6 rounds cover any depth below 64.
 //  SEGMENT : own-segment rows up to i, plus rows of the `lookback` previous
 //            segments (all earlier segments when lookback < 0).
-__device__ inline uint64_t node_visibility(int kind, const int32_t* ids, int W, int lookback,
-                                           int lane, bool& ok) {
+// `id` is this lane's mask id (ids[lane] for lane < W, anything otherwise).
+__device__ inline uint64_t node_visibility(int kind, int id, int W, int lookback, int lane,
+                                           bool& ok) {
   const bool in = lane < W;
+  if (!in) id = 0;
   if (kind == MTP_MASK_CHAIN) {
     ok = true;
     return in ? (~0ull >> (63 - lane)) : 0ull;
   }
-  const int id = in ? ids[lane] : 0;
   if (kind == MTP_MASK_TREE) {
     const bool bad = in && lane >= 1 && (id < 0 || id >= lane);
     ok = __ballot(bad) == 0ull;
@@ -144,5 +145,10 @@ __device__ __forceinline__ Item decode_item(int item, const AttnParams& p) {
 }
 
 __device__ __forceinline__ int num_splits(int L, int S) { return L > 0 ? (L + S - 1) / S : 1; }
+
+// Lane's mask id of sequence b (0 for lanes past the block).
+__device__ __forceinline__ int lane_mask_id(const AttnParams& p, int b, int lane) {
+  return lane < p.W ? p.mask_ids[(size_t)b * p.W + lane] : 0;
+}
 
 }  // namespace mtpv

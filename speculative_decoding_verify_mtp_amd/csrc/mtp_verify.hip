@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "accept_commit.hpp"
+#include "attn_lds.hpp"
 #include "attn_mfma.hpp"
 #include "attn_valu.hpp"
 #include "combine.hpp"
@@ -18,16 +19,23 @@ namespace {
 using namespace mtpv;
 
 // Committed tokens per split when the caller does not fix it: enough work
-// items to fill 256 CUs several times over, but no split shorter than 64 tokens
-// (the partial it writes would rival the K/V it reads) or longer than 2048.
-constexpr long kTargetItems = 2048;
+// items to fill 256 CUs several times over (1024 workgroups of the LDS kernel,
+// 2048 single-wave items otherwise), no longer than 2048 tokens, and at least
+// twice the rows of an item (the partial a split writes, rows x (D+2) x 4
+// bytes, then stays below half of the K/V it reads, split x 4D bytes).
+constexpr long kTargetWorkgroups = 1024;
+constexpr long kTargetWaves = 2048;
 constexpr int kMinSplit = 64;
 constexpr int kMaxSplit = 2048;
 
+enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2 };
+
 struct Plan {
+  Kernel kernel;   // VALU (fp32, or < 16 rows), MFMA with direct loads (D=64), MFMA + LDS ring (D=128)
   bool mfma;       // bf16 with >= 16 rows per KV head
   int g, R;        // group size, rows per KV head (W * g)
   int RB;          // MFMA row tiles per wave (1, 2 or 4)
+  int NR;          // waves per workgroup (LDS kernel; 1 wave per item otherwise)
   int nRB;         // row blocks (MFMA) or row chunks (VALU) per KV head
   int S;           // committed tokens per split
   int max_splits;  // splits of the longest context
@@ -43,7 +51,8 @@ mtp_status check_shape(const mtp_shape* s) {
   if ((int64_t)s->max_ctx_len > (int64_t)s->max_pages_per_seq * MTP_PAGE_SIZE) return MTP_ERR_SHAPE;
   if (s->max_ctx_len > 0 && s->num_pages < 1) return MTP_ERR_SHAPE;  // committed keys need pages
   if (s->seg_lookback < -1) return MTP_ERR_SHAPE;
-  if (s->split_tokens < 0 || s->split_tokens % 32 != 0) return MTP_ERR_SHAPE;
+  if (s->split_tokens < 0 || s->split_tokens % 32 != 0 || s->split_tokens > kMaxSplit)
+    return MTP_ERR_SHAPE;
   if (!(s->scale >= 0.f) || isinf(s->scale)) return MTP_ERR_SHAPE;
   if (s->page_size != MTP_PAGE_SIZE) return MTP_ERR_UNSUPPORTED;
   if (s->D != 64 && s->D != 128) return MTP_ERR_UNSUPPORTED;
@@ -62,21 +71,37 @@ Plan make_plan(const mtp_shape& s) {
   pl.g = s.Hq / s.Hkv;
   pl.R = s.W * pl.g;
   pl.mfma = s.dtype == MTP_BF16 && pl.R >= 16;
-  if (pl.mfma) {
+  pl.NR = 1;
+  const int tiles = (pl.R + 15) / 16;
+  if (pl.mfma && s.D == 128) {
+    // One workgroup of NR waves shares each K/V stage; wave w owns RB row
+    // tiles.  Up to 4 waves x 2 tiles = 128 rows per row block.
+    pl.kernel = kMfmaLds;
+    pl.NR = tiles >= 3 ? 4 : tiles;
+    const int per = (tiles + pl.NR - 1) / pl.NR;
+    pl.RB = per >= 2 ? 2 : 1;
+    pl.nRB = (tiles + pl.NR * pl.RB - 1) / (pl.NR * pl.RB);
+  } else if (pl.mfma) {
     // Row tiles per wave: 1, 2 or 4 (a third tile is padded to four so the
     // K/V stream is still read once).
-    const int tiles = (pl.R + 15) / 16;
+    pl.kernel = kMfmaDirect;
     pl.RB = tiles >= 3 ? 4 : tiles;
     pl.nRB = (tiles + pl.RB - 1) / pl.RB;
   } else {
+    pl.kernel = kValu;
     pl.RB = 0;
     pl.nRB = (pl.R + kValuRows - 1) / kValuRows;
   }
   if (s.split_tokens > 0) {
     pl.S = s.split_tokens;
   } else {
+    const long target = pl.kernel == kMfmaLds ? kTargetWorkgroups : kTargetWaves;
+    const int rows_item = pl.kernel == kMfmaLds ? 16 * pl.NR * pl.RB
+                          : pl.kernel == kMfmaDirect ? 16 * pl.RB : kValuRows;
     const long work = (long)s.B * s.Hkv * pl.nRB * (long)(s.max_ctx_len > 0 ? s.max_ctx_len : 1);
-    int S = pow2_ceil((work + kTargetItems - 1) / kTargetItems);
+    int S = pow2_ceil((work + target - 1) / target);
+    const int floor_rows = pow2_ceil(2L * rows_item);
+    S = S < floor_rows ? floor_rows : S;
     pl.S = S < kMinSplit ? kMinSplit : (S > kMaxSplit ? kMaxSplit : S);
   }
   pl.max_splits = s.max_ctx_len > 0 ? (s.max_ctx_len + pl.S - 1) / pl.S : 1;
@@ -176,7 +201,14 @@ mtp_status verify_attn_phases(int phases, const mtp_shape* shape, const void* q,
   if (phases & kPartial) {
     const long items = (long)pl.max_splits * s.Hkv * pl.nRB;
     const dim3 grid((unsigned)((items + 3) / 4), (unsigned)s.B);
-    if (pl.mfma) {
+    if (pl.kernel == kMfmaLds) {
+      const dim3 wgrid((unsigned)items, (unsigned)s.B);
+      const dim3 wblock(64 * pl.NR);
+      if (pl.RB == 2) attn_partial_lds<2, 4><<<wgrid, wblock, 0, strm>>>(p);
+      else if (pl.NR == 4) attn_partial_lds<1, 4><<<wgrid, wblock, 0, strm>>>(p);
+      else if (pl.NR == 2) attn_partial_lds<1, 2><<<wgrid, wblock, 0, strm>>>(p);
+      else attn_partial_lds<1, 1><<<wgrid, wblock, 0, strm>>>(p);
+    } else if (pl.mfma) {
       if (s.D == 128) {
         if (pl.RB == 4) attn_partial_mfma<128, 4><<<grid, block, 0, strm>>>(p);
         else if (pl.RB == 2) attn_partial_mfma<128, 2><<<grid, block, 0, strm>>>(p);

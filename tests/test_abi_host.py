@@ -64,7 +64,7 @@ def ws(L, s) -> tuple[int, int]:
 @pytest.mark.parametrize("bad,code", [
     (dict(W=0), 2), (dict(W=65), 2), (dict(Hq=6, Hkv=4), 2), (dict(Hkv=0), 2),
     (dict(D=96), 3), (dict(dtype=5), 3), (dict(max_ctx_len=641), 2), (dict(B=-1), 2),
-    (dict(seg_lookback=-2), 2), (dict(split_tokens=48), 2), (dict(scale=-1.0), 2),
+    (dict(seg_lookback=-2), 2), (dict(split_tokens=48), 2), (dict(split_tokens=2080), 2), (dict(scale=-1.0), 2),
     (dict(scale=float("nan")), 2), (dict(num_pages=-1), 2), (dict(num_pages=0), 2),
 ])
 def test_shape_errors_are_reported_on_the_host(L, bad, code):
@@ -103,23 +103,37 @@ def test_empty_batch_needs_no_pointers(L):
 
 def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     """The documented split plan: rows per KV head R = W * g; bf16 with R >= 16
-    runs on MFMA in row blocks of 16, 32 or 64 rows, everything else in chunks of
-    4 rows; the automatic split is the power of two giving about 2048 work
-    items, clamped to [64, 2048] tokens."""
+    runs on MFMA (D=128: workgroups of up to 4 waves x 2 row tiles; D=64: one
+    wave of 1, 2 or 4 row tiles per row block), everything else in chunks of
+    4 rows; the automatic split is the power of two giving about 1024
+    workgroups (LDS kernel) or 2048 waves (the others), at least twice the
+    rows of an item, clamped to [64, 2048] tokens."""
     g = Hq // Hkv
     R = W * g
-    if dtype == lib.MTP_BF16 and R >= 16:
-        tiles = (R + 15) // 16
+    tiles = (R + 15) // 16
+    if dtype == lib.MTP_BF16 and R >= 16 and D == 128:
+        nr = 4 if tiles >= 3 else tiles
+        per = -(-tiles // nr)
+        rb = 2 if per >= 2 else 1
+        nrb = -(-tiles // (nr * rb))
+        items, rows_item = 1024, 16 * nr * rb
+    elif dtype == lib.MTP_BF16 and R >= 16:
         rb = 4 if tiles >= 3 else tiles
         nrb = (tiles + rb - 1) // rb
+        items, rows_item = 2048, 16 * rb
     else:
         nrb = (R + 3) // 4
+        items, rows_item = 2048, 4
+
+    def pow2_ceil(x):
+        p = 1
+        while p < x:
+            p *= 2
+        return p
+
     if split == 0:
         work = B * Hkv * nrb * max(max_ctx, 1)
-        target = -(-work // 2048)
-        S = 1
-        while S < target:
-            S *= 2
+        S = max(pow2_ceil(-(-work // items)), pow2_ceil(2 * rows_item))
         S = min(max(S, 64), 2048)
     else:
         S = split
@@ -137,6 +151,9 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     dict(B=1, W=4, Hq=4, Hkv=4, D=64, dtype=0, max_ctx=256),
     dict(B=3, W=3, Hq=4, Hkv=4, D=128, dtype=1, max_ctx=0),
     dict(B=2, W=8, Hq=8, Hkv=2, D=128, dtype=1, max_ctx=600, split=96),
+    dict(B=2, W=64, Hq=64, Hkv=8, D=128, dtype=1, max_ctx=3000),
+    dict(B=2, W=12, Hq=16, Hkv=4, D=128, dtype=1, max_ctx=3000),
+    dict(B=2, W=12, Hq=16, Hkv=4, D=64, dtype=1, max_ctx=3000),
 ])
 def test_workspace_follows_the_split_plan(L, kw):
     s = lib.VerifyShape(kw["B"], kw["W"], kw["Hq"], kw["Hkv"], kw["D"], 10,
