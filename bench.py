@@ -1,8 +1,9 @@
 """Verify-step benchmark on one MI355X.
 
-One step = the whole verify hot path over one batch of synthetic input:
-split-K verify attention (partial + combine kernels), greedy acceptance and
-KV commit (one fused launch).  Inputs are resident in HBM before timing.
+One step = the whole verify hot path over one batch of synthetic input
+(mtp_verify_step): the split-K verify-attention partial kernel, then one
+launch running the combine beside greedy acceptance and KV commit.  Inputs
+are resident in HBM before timing.
 Cold-cache by default: the KV page pool is replicated R times (R * KV >= 1 GB,
 well above the 256 MB Infinity Cache) and step i reads replica i % R.
 
@@ -195,20 +196,16 @@ def main() -> int:
     bonus = torch.empty(B, dtype=torch.int32, device=dev)
     ctx_out = torch.empty_like(inp["ctx_lens"])
 
-    def launch_step(r: int, phases=("partial", "combine", "accept")):
+    def launch_step(r: int, partial_only: bool = False):
         common = (inp["q"], k_all, v_all, tables[r], inp["ctx_lens"], inp["k_new"], inp["v_new"],
                   inp["mask_kind"], inp["mask_ids"])
-        if "partial" in phases:
+        if partial_only:
             lib.verify_attn(*common, out=out, lse=lse, workspace=workspace, shape=shape,
                             phase="partial")
-        if "combine" in phases:
-            lib.verify_attn(*common, out=out, lse=lse, workspace=workspace, shape=shape,
-                            phase="combine")
-        if "accept" in phases:
-            lib.accept_commit(inp["logits"], inp["draft_ids"], inp["mask_kind"],
-                              inp["mask_ids"], inp["k_new"], inp["v_new"], tables[r],
-                              inp["ctx_lens"], k_all, v_all, accept_len=alen,
-                              accept_path=apath, bonus_id=bonus, ctx_lens_out=ctx_out)
+            return
+        lib.verify_step(*common, inp["logits"], inp["draft_ids"], out=out, lse=lse,
+                        accept_len=alen, accept_path=apath, bonus_id=bonus,
+                        ctx_lens_out=ctx_out, workspace=workspace, shape=shape)
 
     # Launch-bound steps are replayed from HIP graphs: one graph holds R whole
     # steps (one per KV replica), a second holds the R partial-kernel launches
@@ -224,7 +221,7 @@ def main() -> int:
                 launch_step(r)
         with torch.cuda.graph(g_part, stream=cap):
             for r in range(R):
-                launch_step(r, ("partial",))
+                launch_step(r, partial_only=True)
     torch.cuda.synchronize()
 
     reps = max(1, math.ceil(args.steps / R))

@@ -208,6 +208,22 @@ mtp_status mtp_accept_commit(const mtp_shape* shape, const float* logits, int32_
                              const int32_t* ctx_lens_in, int32_t* ctx_lens_out,
                              int32_t skip_root, void* k_cache, void* v_cache, void* stream);
 
+/* The whole verify step in two launches: the split-K partial kernel, then
+ * one launch that runs the combine (out, lse) side by side with acceptance
+ * and commit.  Arguments as for mtp_verify_attn and mtp_accept_commit;
+ * attention reads ctx_lens_in and the cache as they are before the commit.
+ * When ctx_lens_out aliases ctx_lens_in the combine and the commit run as
+ * two launches instead (the combine reads the lengths the commit updates).
+ * Results are those of mtp_verify_attn followed by mtp_accept_commit. */
+mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* ctx_lens_in,
+                           const void* k_new, const void* v_new, const uint8_t* mask_kind,
+                           const int32_t* mask_ids, const float* logits, int32_t V,
+                           const int32_t* draft_ids, float* out, float* lse,
+                           int32_t* accept_len, int32_t* accept_path, int32_t* bonus_id,
+                           int32_t* ctx_lens_out, int32_t skip_root, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Reads (and with clear != 0 resets) the current device's sticky status word
  * into *bits.  Synchronous: waits for all work on the device. */
 mtp_status mtp_get_device_status(uint32_t* bits, int32_t clear);

@@ -246,13 +246,13 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
   block_commit<false>(p, b, f, 0, nullptr, s_src, s_dst, s_meta);
 }
 
-__global__ __launch_bounds__(256) void accept_commit_kernel(AcceptParams ap, CommitParams cp) {
+// Acceptance then commit of sequence b by one 256-thread workgroup.
+__device__ inline void accept_commit_seq(const AcceptParams& ap, const CommitParams& cp, int b) {
   __shared__ int s_tgt[MTP_MAX_W];
   __shared__ int s_path[MTP_MAX_W];
   __shared__ int s_src[MTP_MAX_W];
   __shared__ int s_dst[MTP_MAX_W];
   __shared__ int s_meta[2];
-  const int b = blockIdx.x;
   Prefetch f{};
   if (threadIdx.x < kWave) f = prefetch_inputs(ap, &cp, b);
   block_argmax(ap, b, s_tgt);
@@ -261,6 +261,10 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptParams ap, Com
   if (threadIdx.x < kWave) a = wave_accept(ap, b, f, s_tgt, s_path);
   __syncthreads();
   block_commit<true>(cp, b, f, a, s_path, s_src, s_dst, s_meta);
+}
+
+__global__ __launch_bounds__(256) void accept_commit_kernel(AcceptParams ap, CommitParams cp) {
+  accept_commit_seq(ap, cp, blockIdx.x);
 }
 
 }  // namespace mtpv

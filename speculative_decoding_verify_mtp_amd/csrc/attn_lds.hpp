@@ -85,7 +85,7 @@ __device__ __forceinline__ void wait_vmem_barrier() {
 // may stay in flight, then barrier.
 template <int PER>
 __device__ __forceinline__ void wait_stage_barrier(int n) {
-  static_assert(kLdsStages <= 5, "wait counts below cover up to three later stages");
+  // covers up to three later stages (rings of at most five stages)
   if (n <= 0)
     wait_vmem_barrier<0>();
   else if (n == 1)
@@ -113,31 +113,14 @@ void attn_partial_lds(AttnParams p) {
   const int b = blockIdx.y;
   const Item it = decode_item(blockIdx.x, p);
   if (it.split >= p.max_splits) return;  // uniform over the workgroup
-  const int L = p.ctx_lens[b];
-  if (L < 0 || L > p.max_ctx) return;
-  const int ns = num_splits(L, p.S);
-  if (it.split >= ns) return;
   const int start = it.split * p.S;
-  const int end = min(L, start + p.S);
-  const bool last = it.split == ns - 1;
 
-  const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache) + (size_t)it.kvh * D;
-  const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache) + (size_t)it.kvh * D;
-  const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (size_t)it.kvh * D;
-  const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (size_t)it.kvh * D;
-  const size_t slot_stride = (size_t)p.Hkv * D;
-
-  // ---- set-up loads: page indices of the split, Q operands, in-block mask
-  const int npg = (end - start + kPage - 1) / kPage;
+  // Loads that do not depend on the context length go out together with it:
+  // the split's page indices (bounded by the block table) and Q.
   const int32_t* btrow = p.block_table + (size_t)b * p.max_pages + start / kPage;
-  int pr0 = lane < npg ? btrow[lane] : 0;
-  int pr1 = lane + 64 < npg ? btrow[lane + 64] : 0;
-  bool bad = (lane < npg && (unsigned)pr0 >= (unsigned)p.num_pages) ||
-             (lane + 64 < npg && (unsigned)pr1 >= (unsigned)p.num_pages);
-  bad = __ballot(bad) != 0ull;
-  if ((unsigned)pr0 >= (unsigned)p.num_pages) pr0 = 0;
-  if ((unsigned)pr1 >= (unsigned)p.num_pages) pr1 = 0;
-
+  const int pavail = p.max_pages - start / kPage;
+  int pr0 = lane < pavail ? btrow[lane] : 0;
+  int pr1 = lane + 64 < pavail ? btrow[lane + 64] : 0;
   const int row_tile0 = (it.rb * NR + wv) * RB;
   bf16x8 qf[RB][NC];
 #pragma unroll
@@ -155,6 +138,27 @@ void attn_partial_lds(AttnParams p) {
       for (int m = 0; m < NC; ++m) qf[k][m] = bf16x8{};
     }
   }
+
+  const int L = p.ctx_lens[b];
+  if (L < 0 || L > p.max_ctx) return;
+  const int ns = num_splits(L, p.S);
+  if (it.split >= ns) return;
+  const int end = min(L, start + p.S);
+  const bool last = it.split == ns - 1;
+
+  const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache) + (size_t)it.kvh * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache) + (size_t)it.kvh * D;
+  const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (size_t)it.kvh * D;
+  const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (size_t)it.kvh * D;
+  const size_t slot_stride = (size_t)p.Hkv * D;
+
+  // ---- page indices of the committed range: validate, clamp
+  const int npg = (end - start + kPage - 1) / kPage;
+  bool bad = (lane < npg && (unsigned)pr0 >= (unsigned)p.num_pages) ||
+             (lane + 64 < npg && (unsigned)pr1 >= (unsigned)p.num_pages);
+  bad = __ballot(bad) != 0ull;
+  if ((unsigned)pr0 >= (unsigned)p.num_pages) pr0 = 0;
+  if ((unsigned)pr1 >= (unsigned)p.num_pages) pr1 = 0;
 
   int ntail = 0;
   uint64_t vrow[RB];

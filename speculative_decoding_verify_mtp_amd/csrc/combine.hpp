@@ -10,16 +10,21 @@
 // four group sums are folded with two shuffles.
 #pragma once
 
+#include "accept_commit.hpp"
+#include "attn_stream.hpp"
 #include "common.hpp"
 
 namespace mtpv {
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnParams p) {
+// kStream = false: partials of the split kernels, [B, splits, Hkv, R] rows.
+// kStream = true : pieces of the stream kernel, [pieces, rows_block] rows,
+//                  located through the segment table.
+template <int D, bool kStream>
+__device__ inline void combine_rows(const AttnParams& p, const StreamParams& sp, unsigned block) {
   constexpr int VPL = D / 16;  // accumulators per lane per split
   const int lane = threadIdx.x & 63;
   const int gq = lane >> 4, gl = lane & 15;
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t row = (size_t)block * 4 + (threadIdx.x >> 6);
   if (row >= (size_t)p.B * p.W * p.Hq) return;
   const int h = (int)(row % p.Hq);
   const size_t bw = row / p.Hq;
@@ -27,6 +32,33 @@ __global__ __launch_bounds__(256) void attn_combine(AttnParams p) {
   const int b = (int)(bw / p.W);
   const int kvh = h / p.g;
   const int rho = w * p.g + (h - kvh * p.g);
+
+  // Loads that need neither the context length nor the split states go out
+  // first: for the split layout, the accumulators of the first 32 splits of
+  // the launch-wide split count (splits past this row's count are dropped
+  // by selection, never by a zero weight: stale workspace may hold NaN).
+  constexpr int kBatch = 8;  // splits per 16-lane group in flight
+  size_t base0 = 0, sstride0 = 0;
+  if constexpr (!kStream) {
+    base0 = (((size_t)b * p.max_splits) * p.Hkv + kvh) * (size_t)p.R + rho;
+    sstride0 = (size_t)p.Hkv * p.R;
+  }
+  float4 v[kBatch][VPL / 4];
+  float m_spec = neg_inf(), l_spec = 0.f;  // split state of split `lane`
+  if constexpr (!kStream) {
+    if (lane < p.max_splits) {
+      m_spec = p.part_ml[2 * (base0 + lane * sstride0)];
+      l_spec = p.part_ml[2 * (base0 + lane * sstride0) + 1];
+    }
+    const int nspec = p.max_splits < 4 * kBatch ? p.max_splits : 4 * kBatch;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sl = 4 * u + gq < nspec ? 4 * u + gq : 0;
+      const float4* src = reinterpret_cast<const float4*>(p.part_acc + (base0 + sl * sstride0) * D + gl * VPL);
+#pragma unroll
+      for (int j = 0; j < VPL / 4; ++j) v[u][j] = src[j];
+    }
+  }
 
   const int L = p.ctx_lens[b];
   bool ok;
@@ -40,20 +72,49 @@ __global__ __launch_bounds__(256) void attn_combine(AttnParams p) {
     if (p.lse != nullptr && lane == 0) p.lse[row] = qnan();
     return;
   }
-  const int ns = num_splits(L, p.S);
-  const size_t base = (((size_t)b * p.max_splits) * p.Hkv + kvh) * (size_t)p.R + rho;
-  const size_t sstride = (size_t)p.Hkv * p.R;
+  int ns;
+  size_t base, sstride;
+  if constexpr (kStream) {
+    const int rb = rho / sp.rows_block;
+    const int sigma = b * sp.nseg + kvh * p.nRB + rb;
+    ns = sp.seg_info[2 * sigma + 1];
+    base = (size_t)sp.seg_info[2 * sigma] * sp.rows_block + (rho - rb * sp.rows_block);
+    sstride = (size_t)sp.rows_block;
+  } else {
+    ns = num_splits(L, p.S);
+    base = (((size_t)b * p.max_splits) * p.Hkv + kvh) * (size_t)p.R + rho;
+    sstride = (size_t)p.Hkv * p.R;
+  }
+
+  // Stream layout: the pieces are known now; their accumulators are requested
+  // before the split states come back (they do not depend on the max).
+  const int nfast = ns < 4 * kBatch ? ns : 4 * kBatch;
+  if constexpr (kStream) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sl = 4 * u + gq < nfast ? 4 * u + gq : 0;
+      const float4* src = reinterpret_cast<const float4*>(p.part_acc + (base + sl * sstride) * D + gl * VPL);
+#pragma unroll
+      for (int j = 0; j < VPL / 4; ++j) v[u][j] = src[j];
+    }
+  }
 
   // pass 1: reference max and denominator, one split per lane
-  float M = neg_inf();
-  for (int s = lane; s < ns; s += kWave) M = fmaxf(M, p.part_ml[2 * (base + s * sstride)]);
+  if constexpr (kStream) {
+    if (lane < ns) {
+      m_spec = p.part_ml[2 * (base + lane * sstride)];
+      l_spec = p.part_ml[2 * (base + lane * sstride) + 1];
+    }
+  }
+  const bool have = lane < ns;
+  float M = have ? m_spec : neg_inf();
+  for (int s = lane + kWave; s < ns; s += kWave) M = fmaxf(M, p.part_ml[2 * (base + s * sstride)]);
   M = wave_max(M);
-  float wl = 0.f, wlane = 0.f;  // weight of split `lane` (first 64 splits)
-  for (int s = lane; s < ns; s += kWave) {
+  const float wlane = have ? fast_exp2(m_spec - M) : 0.f;  // weight of split `lane`
+  float wl = have ? wlane * l_spec : 0.f;
+  for (int s = lane + kWave; s < ns; s += kWave) {
     const size_t i = base + s * sstride;
-    const float wt = fast_exp2(p.part_ml[2 * i] - M);
-    if (s == lane) wlane = wt;
-    wl += wt * p.part_ml[2 * i + 1];
+    wl += fast_exp2(p.part_ml[2 * i] - M) * p.part_ml[2 * i + 1];
   }
   const float den = wave_sum(wl);
 
@@ -61,19 +122,42 @@ __global__ __launch_bounds__(256) void attn_combine(AttnParams p) {
   float a[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) a[j] = 0.f;
-  const int nfast = ns < kWave ? ns : kWave;
-  for (int s0 = 0; s0 < nfast; s0 += 4) {  // splits whose weight sits in a lane
-    const int s = s0 + gq;
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int s = 4 * u + gq;
     const float wt = __shfl(wlane, s & 63);
     if (s < nfast) {
-      const float4* src = reinterpret_cast<const float4*>(p.part_acc + (base + s * sstride) * D + gl * VPL);
 #pragma unroll
       for (int j = 0; j < VPL / 4; ++j) {
-        const float4 v = src[j];
-        a[4 * j] = fmaf(wt, v.x, a[4 * j]);
-        a[4 * j + 1] = fmaf(wt, v.y, a[4 * j + 1]);
-        a[4 * j + 2] = fmaf(wt, v.z, a[4 * j + 2]);
-        a[4 * j + 3] = fmaf(wt, v.w, a[4 * j + 3]);
+        a[4 * j] = fmaf(wt, v[u][j].x, a[4 * j]);
+        a[4 * j + 1] = fmaf(wt, v[u][j].y, a[4 * j + 1]);
+        a[4 * j + 2] = fmaf(wt, v[u][j].z, a[4 * j + 2]);
+        a[4 * j + 3] = fmaf(wt, v[u][j].w, a[4 * j + 3]);
+      }
+    }
+  }
+  // splits 32..63 (weights in lanes), in batches of eight per group
+  const int nlane = ns < kWave ? ns : kWave;
+  for (int s0 = 4 * kBatch; s0 < nlane; s0 += 4 * kBatch) {
+    float wt[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = s0 + 4 * u + gq;
+      wt[u] = __shfl(wlane, s & 63);
+      const int sl = s < nlane ? s : 0;
+      if (s >= nlane) wt[u] = 0.f;
+      const float4* src = reinterpret_cast<const float4*>(p.part_acc + (base + sl * sstride) * D + gl * VPL);
+#pragma unroll
+      for (int j = 0; j < VPL / 4; ++j) v[u][j] = src[j];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+#pragma unroll
+      for (int j = 0; j < VPL / 4; ++j) {
+        a[4 * j] = fmaf(wt[u], v[u][j].x, a[4 * j]);
+        a[4 * j + 1] = fmaf(wt[u], v[u][j].y, a[4 * j + 1]);
+        a[4 * j + 2] = fmaf(wt[u], v[u][j].z, a[4 * j + 2]);
+        a[4 * j + 3] = fmaf(wt[u], v[u][j].w, a[4 * j + 3]);
       }
     }
   }
@@ -103,6 +187,25 @@ __global__ __launch_bounds__(256) void attn_combine(AttnParams p) {
       dst[j] = make_float4(a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv, a[4 * j + 3] * inv);
   }
   if (p.lse != nullptr && lane == 0) p.lse[row] = (M + log2f(den)) * kLn2;
+}
+
+template <int D, bool kStream>
+__global__ __launch_bounds__(256) void attn_combine(AttnParams p, StreamParams sp) {
+  combine_rows<D, kStream>(p, sp, blockIdx.x);
+}
+
+// The step's second launch: combine workgroups for every output row, then
+// one acceptance + commit workgroup per sequence.  The two parts touch
+// disjoint data (the commit writes cache slots at or past each context
+// length and ctx_lens_out, which must not alias the ctx_lens the combine
+// reads), so they run side by side.
+template <int D, bool kStream>
+__global__ __launch_bounds__(256) void finish_kernel(AttnParams p, StreamParams sp, AcceptParams ap,
+                                                     CommitParams cp, unsigned combine_blocks) {
+  if (blockIdx.x < combine_blocks)
+    combine_rows<D, kStream>(p, sp, blockIdx.x);
+  else
+    accept_commit_seq(ap, cp, (int)(blockIdx.x - combine_blocks));
 }
 
 }  // namespace mtpv

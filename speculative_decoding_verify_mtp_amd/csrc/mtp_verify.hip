@@ -9,6 +9,7 @@
 #include "accept_commit.hpp"
 #include "attn_lds.hpp"
 #include "attn_mfma.hpp"
+#include "attn_stream.hpp"
 #include "attn_valu.hpp"
 #include "combine.hpp"
 #include "common.hpp"
@@ -28,7 +29,16 @@ constexpr long kTargetWaves = 2048;
 constexpr int kMinSplit = 64;
 constexpr int kMaxSplit = 2048;
 
-enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2 };
+enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3 };
+
+// Stream kernel: persistent grid sized for gfx950's 256 CUs (two workgroups
+// per CU at one row tile per wave, one at two), each workgroup streaming at
+// least kMinStreamStages stages.
+constexpr int kCUs = 256;
+constexpr long kMinStreamStages = 2;
+// A handful of sequences is balanced by the split plan already, and the
+// stream kernel's per-workgroup set-up would dominate their short ranges.
+constexpr int kStreamMinB = 8;
 
 struct Plan {
   Kernel kernel;   // VALU (fp32, or < 16 rows), MFMA with direct loads (D=64), MFMA + LDS ring (D=128)
@@ -39,7 +49,9 @@ struct Plan {
   int nRB;         // row blocks (MFMA) or row chunks (VALU) per KV head
   int S;           // committed tokens per split
   int max_splits;  // splits of the longest context
-  size_t acc_bytes, ml_offset, ml_bytes;
+  int G;           // stream kernel: workgroups
+  int nts, nseg, rows_block;
+  size_t acc_bytes, ml_offset, ml_bytes, seg_offset, seg_bytes;
 };
 
 mtp_status check_shape(const mtp_shape* s) {
@@ -105,10 +117,30 @@ Plan make_plan(const mtp_shape& s) {
     pl.S = S < kMinSplit ? kMinSplit : (S > kMaxSplit ? kMaxSplit : S);
   }
   pl.max_splits = s.max_ctx_len > 0 ? (s.max_ctx_len + pl.S - 1) / pl.S : 1;
-  const size_t rows = (size_t)s.B * pl.max_splits * s.Hkv * pl.R;
+  pl.G = 0;
+  pl.nts = (s.W + 31) / 32;
+  pl.nseg = s.Hkv * pl.nRB;
+  pl.rows_block = 16 * pl.NR * pl.RB;
+  size_t rows = (size_t)s.B * pl.max_splits * s.Hkv * pl.R;
+  if (pl.kernel == kMfmaLds && s.B >= kStreamMinB && s.B <= kStreamMaxB) {
+    // stage count bound from max_ctx_len; the device splits the true count
+    const long seg_stages = (long)(s.max_ctx_len + 31) / 32 + pl.nts;
+    const long upper = (long)s.B * pl.nseg * seg_stages;
+    if (upper < (1L << 30)) {
+      pl.kernel = kMfmaStream;
+      const long slots = (long)kCUs * (pl.RB == 1 ? 2 : 1);
+      long per = s.split_tokens > 0 ? s.split_tokens / 32 : kMinStreamStages;
+      long G = (upper + per - 1) / per;
+      if (s.split_tokens == 0 && G > slots) G = slots;
+      pl.G = (int)(G < 1 ? 1 : (G > 65535 ? 65535 : G));
+      rows = ((size_t)pl.G + (size_t)s.B * pl.nseg) * pl.rows_block;
+    }
+  }
   pl.acc_bytes = rows * s.D * sizeof(float);
   pl.ml_offset = (pl.acc_bytes + 255) & ~(size_t)255;
   pl.ml_bytes = rows * 2 * sizeof(float);
+  pl.seg_offset = (pl.ml_offset + pl.ml_bytes + 255) & ~(size_t)255;
+  pl.seg_bytes = pl.kernel == kMfmaStream ? (size_t)s.B * pl.nseg * 2 * sizeof(int) : 0;
   return pl;
 }
 
@@ -139,7 +171,7 @@ mtp_status mtp_verify_attn_workspace_size(const mtp_shape* shape, size_t* bytes)
   if (st != MTP_OK) return st;
   if (bytes == nullptr) return MTP_ERR_NULL;
   const Plan pl = make_plan(*shape);
-  *bytes = pl.ml_offset + pl.ml_bytes;
+  *bytes = pl.seg_offset + pl.seg_bytes;
   return MTP_OK;
 }
 
@@ -149,12 +181,17 @@ namespace {
 
 enum Phase { kPartial = 1, kCombine = 2, kBoth = 3 };
 
-mtp_status verify_attn_phases(int phases, const mtp_shape* shape, const void* q,
-                              const void* k_cache, const void* v_cache,
-                              const int32_t* block_table, const int32_t* ctx_lens,
-                              const void* k_new, const void* v_new, const uint8_t* mask_kind,
-                              const int32_t* mask_ids, float* out, float* lse, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+struct Attn {
+  Plan pl;
+  AttnParams p;
+  StreamParams sp;
+};
+
+mtp_status build_attn(const mtp_shape* shape, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
+                      const void* k_new, const void* v_new, const uint8_t* mask_kind,
+                      const int32_t* mask_ids, float* out, float* lse, void* workspace,
+                      size_t workspace_bytes, Attn& a) {
   const mtp_status st = check_shape(shape);
   if (st != MTP_OK) return st;
   const mtp_shape& s = *shape;
@@ -162,11 +199,11 @@ mtp_status verify_attn_phases(int phases, const mtp_shape* shape, const void* q,
   if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !k_new || !v_new || !mask_kind ||
       !mask_ids || !out || !workspace)
     return MTP_ERR_NULL;
-  const Plan pl = make_plan(s);
-  if (workspace_bytes < pl.ml_offset + pl.ml_bytes || ((uintptr_t)workspace & 15) != 0)
+  a.pl = make_plan(s);
+  const Plan& pl = a.pl;
+  if (workspace_bytes < pl.seg_offset + pl.seg_bytes || ((uintptr_t)workspace & 15) != 0)
     return MTP_ERR_WORKSPACE;
-
-  AttnParams p;
+  AttnParams& p = a.p;
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
@@ -195,21 +232,37 @@ mtp_status verify_attn_phases(int phases, const mtp_shape* shape, const void* q,
   p.lookback = s.seg_lookback;
   const float scale = s.scale > 0.f ? s.scale : 1.f / sqrtf((float)s.D);
   p.scale_log2 = scale * kLog2e;
+  a.sp.seg_info = reinterpret_cast<int*>(static_cast<char*>(workspace) + pl.seg_offset);
+  a.sp.nts = pl.nts;
+  a.sp.nseg = pl.nseg;
+  a.sp.rows_block = pl.rows_block;
+  return MTP_OK;
+}
 
-  hipStream_t strm = static_cast<hipStream_t>(stream);
+void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm) {
+  const Plan& pl = a.pl;
+  const AttnParams& p = a.p;
+  const StreamParams& sp = a.sp;
   const dim3 block(256);
-  if (phases & kPartial) {
-    const long items = (long)pl.max_splits * s.Hkv * pl.nRB;
-    const dim3 grid((unsigned)((items + 3) / 4), (unsigned)s.B);
-    if (pl.kernel == kMfmaLds) {
-      const dim3 wgrid((unsigned)items, (unsigned)s.B);
-      const dim3 wblock(64 * pl.NR);
-      if (pl.RB == 2) attn_partial_lds<2, 4><<<wgrid, wblock, 0, strm>>>(p);
-      else if (pl.NR == 4) attn_partial_lds<1, 4><<<wgrid, wblock, 0, strm>>>(p);
-      else if (pl.NR == 2) attn_partial_lds<1, 2><<<wgrid, wblock, 0, strm>>>(p);
-      else attn_partial_lds<1, 1><<<wgrid, wblock, 0, strm>>>(p);
-    } else if (pl.mfma) {
-      if (s.D == 128) {
+  const long items = (long)pl.max_splits * p.Hkv * pl.nRB;
+  if (pl.kernel == kMfmaStream) {
+    const dim3 sgrid((unsigned)pl.G);
+    const dim3 sblock(64 * pl.NR);
+    if (pl.RB == 2) attn_partial_stream<2, 4><<<sgrid, sblock, 0, strm>>>(p, sp);
+    else if (pl.NR == 4) attn_partial_stream<1, 4><<<sgrid, sblock, 0, strm>>>(p, sp);
+    else if (pl.NR == 2) attn_partial_stream<1, 2><<<sgrid, sblock, 0, strm>>>(p, sp);
+    else attn_partial_stream<1, 1><<<sgrid, sblock, 0, strm>>>(p, sp);
+  } else if (pl.kernel == kMfmaLds) {
+    const dim3 wgrid((unsigned)items, (unsigned)B);
+    const dim3 wblock(64 * pl.NR);
+    if (pl.RB == 2) attn_partial_lds<2, 4><<<wgrid, wblock, 0, strm>>>(p);
+    else if (pl.NR == 4) attn_partial_lds<1, 4><<<wgrid, wblock, 0, strm>>>(p);
+    else if (pl.NR == 2) attn_partial_lds<1, 2><<<wgrid, wblock, 0, strm>>>(p);
+    else attn_partial_lds<1, 1><<<wgrid, wblock, 0, strm>>>(p);
+  } else {
+    const dim3 grid((unsigned)((items + 3) / 4), (unsigned)B);
+    if (pl.kernel == kMfmaDirect) {
+      if (D == 128) {
         if (pl.RB == 4) attn_partial_mfma<128, 4><<<grid, block, 0, strm>>>(p);
         else if (pl.RB == 2) attn_partial_mfma<128, 2><<<grid, block, 0, strm>>>(p);
         else attn_partial_mfma<128, 1><<<grid, block, 0, strm>>>(p);
@@ -218,20 +271,40 @@ mtp_status verify_attn_phases(int phases, const mtp_shape* shape, const void* q,
         else if (pl.RB == 2) attn_partial_mfma<64, 2><<<grid, block, 0, strm>>>(p);
         else attn_partial_mfma<64, 1><<<grid, block, 0, strm>>>(p);
       }
-    } else if (s.dtype == MTP_F32) {
-      if (s.D == 128) attn_partial_valu<float, 128><<<grid, block, 0, strm>>>(p);
+    } else if (dtype == MTP_F32) {
+      if (D == 128) attn_partial_valu<float, 128><<<grid, block, 0, strm>>>(p);
       else attn_partial_valu<float, 64><<<grid, block, 0, strm>>>(p);
     } else {
-      if (s.D == 128) attn_partial_valu<uint16_t, 128><<<grid, block, 0, strm>>>(p);
+      if (D == 128) attn_partial_valu<uint16_t, 128><<<grid, block, 0, strm>>>(p);
       else attn_partial_valu<uint16_t, 64><<<grid, block, 0, strm>>>(p);
     }
   }
-  if (phases & kCombine) {
-    const size_t rows = (size_t)s.B * s.W * s.Hq;
-    const dim3 cgrid((unsigned)((rows + 3) / 4));
-    if (s.D == 128) attn_combine<128><<<cgrid, block, 0, strm>>>(p);
-    else attn_combine<64><<<cgrid, block, 0, strm>>>(p);
-  }
+}
+
+unsigned combine_blocks(const AttnParams& p) {
+  return (unsigned)(((size_t)p.B * p.W * p.Hq + 3) / 4);
+}
+
+void launch_combine(const Attn& a, int D, hipStream_t strm) {
+  const dim3 cgrid(combine_blocks(a.p)), block(256);
+  if (a.pl.kernel == kMfmaStream) attn_combine<128, true><<<cgrid, block, 0, strm>>>(a.p, a.sp);
+  else if (D == 128) attn_combine<128, false><<<cgrid, block, 0, strm>>>(a.p, a.sp);
+  else attn_combine<64, false><<<cgrid, block, 0, strm>>>(a.p, a.sp);
+}
+
+mtp_status verify_attn_phases(int phases, const mtp_shape* shape, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens,
+                              const void* k_new, const void* v_new, const uint8_t* mask_kind,
+                              const int32_t* mask_ids, float* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Attn a;
+  const mtp_status st = build_attn(shape, q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new,
+                                   mask_kind, mask_ids, out, lse, workspace, workspace_bytes, a);
+  if (st != MTP_OK || shape->B == 0) return st;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (phases & kPartial) launch_partial(a, shape->D, shape->dtype, shape->B, strm);
+  if (phases & kCombine) launch_combine(a, shape->D, strm);
   return launch_status();
 }
 
@@ -351,6 +424,44 @@ mtp_status mtp_accept_commit(const mtp_shape* shape, const float* logits, int32_
                    ctx_lens_out, skip_root, k_cache, v_cache, true, cp);
   if (st != MTP_OK || shape->B == 0) return st;
   accept_commit_kernel<<<dim3(shape->B), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(ap, cp);
+  return launch_status();
+}
+
+mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* ctx_lens_in,
+                           const void* k_new, const void* v_new, const uint8_t* mask_kind,
+                           const int32_t* mask_ids, const float* logits, int32_t V,
+                           const int32_t* draft_ids, float* out, float* lse,
+                           int32_t* accept_len, int32_t* accept_path, int32_t* bonus_id,
+                           int32_t* ctx_lens_out, int32_t skip_root, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Attn a;
+  mtp_status st = build_attn(shape, q, k_cache, v_cache, block_table, ctx_lens_in, k_new, v_new,
+                             mask_kind, mask_ids, out, lse, workspace, workspace_bytes, a);
+  if (st != MTP_OK) return st;
+  AcceptParams ap;
+  st = fill_accept(shape, logits, V, draft_ids, mask_kind, mask_ids, accept_len, accept_path,
+                   bonus_id, ap);
+  if (st != MTP_OK) return st;
+  CommitParams cp;
+  st = fill_commit(shape, k_new, v_new, accept_len, accept_path, block_table, ctx_lens_in,
+                   ctx_lens_out, skip_root, k_cache, v_cache, true, cp);
+  if (st != MTP_OK || shape->B == 0) return st;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  launch_partial(a, shape->D, shape->dtype, shape->B, strm);
+  if (ctx_lens_out == ctx_lens_in) {  // the combine reads what the commit writes: serialise
+    launch_combine(a, shape->D, strm);
+    accept_commit_kernel<<<dim3(shape->B), dim3(256), 0, strm>>>(ap, cp);
+  } else {
+    const unsigned cb = combine_blocks(a.p);
+    const dim3 fgrid(cb + (unsigned)shape->B), block(256);
+    if (a.pl.kernel == kMfmaStream)
+      finish_kernel<128, true><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, cb);
+    else if (shape->D == 128)
+      finish_kernel<128, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, cb);
+    else
+      finish_kernel<64, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, cb);
+  }
   return launch_status();
 }
 

@@ -23,7 +23,8 @@ DEV_BAD_MASK, DEV_BAD_CTX, DEV_BAD_PAGE, DEV_BAD_ACCEPT = 1, 2, 4, 8
 
 EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_size",
            "mtp_verify_attn", "mtp_verify_attn_partial", "mtp_verify_attn_combine",
-           "mtp_accept", "mtp_kv_commit", "mtp_accept_commit", "mtp_get_device_status")
+           "mtp_accept", "mtp_kv_commit", "mtp_accept_commit", "mtp_verify_step",
+           "mtp_get_device_status")
 _ATTN_FN = {"both": "mtp_verify_attn", "partial": "mtp_verify_attn_partial",
             "combine": "mtp_verify_attn_combine"}
 
@@ -73,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.mtp_accept_commit.restype = _i32
     lib.mtp_accept_commit.argtypes = ([sp, _vp, _i32] + [_vp] * 6 + [_vp] * 5
                                       + [_i32, _vp, _vp, _vp])
+    lib.mtp_verify_step.restype = _i32
+    lib.mtp_verify_step.argtypes = ([sp] + [_vp] * 10 + [_i32] + [_vp] * 7 + [_i32, _vp, _sz, _vp])
     lib.mtp_get_device_status.restype = _i32
     lib.mtp_get_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i32]
     if lib.mtp_abi_version() != 1:
@@ -248,6 +251,43 @@ def accept_commit(logits, draft_ids, mask_kind, mask_ids, k_new, v_new, block_ta
         _ptr(block_table), _ptr(ctx_lens_in), _ptr(ctx_lens_out), int(bool(skip_root)),
         _ptr(k_cache), _ptr(v_cache), _stream(stream)))
     return accept_len, accept_path, bonus_id, ctx_lens_out
+
+
+def verify_step(q, k_cache, v_cache, block_table, ctx_lens_in, k_new, v_new, mask_kind, mask_ids,
+                logits, draft_ids, *, out=None, lse=None, want_lse=True, accept_len=None,
+                accept_path=None, bonus_id=None, ctx_lens_out=None, skip_root=False,
+                workspace=None, shape=None, max_ctx_len=None, scale=0.0, seg_lookback=-1,
+                split_tokens=0, stream=None):
+    """The whole verify step (attention, acceptance, commit) in two launches.
+
+    Returns (out, lse, accept_len, accept_path, bonus_id, ctx_lens_out)."""
+    lib = load()
+    if shape is None:
+        shape = shape_of(q, k_cache, block_table, max_ctx_len=max_ctx_len, scale=scale,
+                         seg_lookback=seg_lookback, split_tokens=split_tokens)
+    B, W, Hq, D = q.shape
+    dev = q.device
+    V = logits.shape[2]
+    if out is None:
+        out = torch.empty((B, W, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, W, Hq), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    accept_path = (torch.empty((B, W), dtype=torch.int32, device=dev) if accept_path is None
+                   else accept_path)
+    bonus_id = torch.empty(B, dtype=torch.int32, device=dev) if bonus_id is None else bonus_id
+    if ctx_lens_out is None:
+        ctx_lens_out = torch.empty_like(ctx_lens_in)
+    cs = shape.c()
+    _check("mtp_verify_step", lib.mtp_verify_step(
+        ctypes.byref(cs), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(ctx_lens_in), _ptr(k_new), _ptr(v_new), _ptr(mask_kind), _ptr(mask_ids),
+        _ptr(logits), V, _ptr(draft_ids), _ptr(out), _ptr(lse), _ptr(accept_len),
+        _ptr(accept_path), _ptr(bonus_id), _ptr(ctx_lens_out), int(bool(skip_root)),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse, accept_len, accept_path, bonus_id, ctx_lens_out
 
 
 def device_status(clear: bool = True) -> int:

@@ -139,8 +139,21 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
         S = split
     ns = -(-max_ctx // S) if max_ctx > 0 else 1
     rows = B * ns * Hkv * R
+    seg = 0
+    if dtype == lib.MTP_BF16 and R >= 16 and D == 128 and 8 <= B <= 1024:
+        # stream kernel: G persistent workgroups, pieces <= G + segments
+        nseg = Hkv * nrb
+        upper = B * nseg * (-(-max_ctx // 32) + -(-W // 32))
+        per = split // 32 if split else 2
+        G = -(-upper // per)
+        if not split:
+            G = min(G, 256 * (2 if rb == 1 else 1))
+        G = max(1, min(G, 65535))
+        rows = (G + B * nseg) * rows_item
+        seg = B * nseg * 8
     acc = rows * D * 4
-    return ((acc + 255) // 256) * 256 + rows * 8
+    a256 = lambda x: ((x + 255) // 256) * 256
+    return a256(a256(acc) + rows * 8) + seg
 
 
 @pytest.mark.parametrize("kw", [
@@ -154,6 +167,9 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     dict(B=2, W=64, Hq=64, Hkv=8, D=128, dtype=1, max_ctx=3000),
     dict(B=2, W=12, Hq=16, Hkv=4, D=128, dtype=1, max_ctx=3000),
     dict(B=2, W=12, Hq=16, Hkv=4, D=64, dtype=1, max_ctx=3000),
+    dict(B=1100, W=4, Hq=4, Hkv=1, D=128, dtype=1, max_ctx=300),
+    dict(B=3, W=33, Hq=8, Hkv=2, D=128, dtype=1, max_ctx=5000, split=256),
+    dict(B=9, W=33, Hq=8, Hkv=2, D=128, dtype=1, max_ctx=5000, split=256),
 ])
 def test_workspace_follows_the_split_plan(L, kw):
     s = lib.VerifyShape(kw["B"], kw["W"], kw["Hq"], kw["Hkv"], kw["D"], 10,

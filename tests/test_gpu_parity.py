@@ -72,6 +72,27 @@ def test_split_size_does_not_change_the_result(split):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"split {split}")
 
 
+def test_batch_above_the_stream_table_uses_per_split_items():
+    """More than 1024 sequences: the per-split LDS kernel instead of the
+    stream schedule (its stage table holds 1024 sequences)."""
+    wl = W_("b1100", B=1100, Hq=4, Hkv=1, W=4, ctx_lo=0, ctx_hi=40, masks="mixed", spare_pages=8)
+    inp = gpu_inputs(wl, 6)
+    out, lse = run_attn(inp)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what="B=1100")
+
+
+@pytest.mark.parametrize("split", [32, 256, 1024])
+def test_stream_work_split_does_not_change_the_result(split):
+    """Workgroups of 1, 8 or 32 stages: ranges start and end inside
+    segments, pieces per segment vary."""
+    wl = W_("stream", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=1500, masks="mixed")
+    inp = gpu_inputs(wl, 13)
+    out, lse = run_attn(inp, split_tokens=split)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"stream split {split}")
+
+
 def test_loose_max_ctx_len_bound():
     """max_ctx_len only sizes the split plan; a loose bound gives the same result."""
     wl = W_("loose", B=2, Hq=8, Hkv=2, W=8, ctx_lo=10, ctx_hi=300, masks="tree")
@@ -319,3 +340,40 @@ def test_empty_batch_is_a_no_op():
                                e(inp["mask_kind"]), e(inp["mask_ids"]), max_ctx_len=10)
     torch.cuda.synchronize()
     assert out.numel() == 0
+
+
+# ----------------------------------------------------------------------------
+# the whole step in two launches
+# ----------------------------------------------------------------------------
+
+STEP = [
+    W_("step_mixed_b9", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=700, masks="mixed"),
+    W_("step_chain_b1", B=1, Hq=20, Hkv=5, W=8, ctx_lo=600, ctx_hi=600),
+    W_("step_segment_d64", B=3, Hq=16, Hkv=16, D=64, W=16, ctx_lo=30, ctx_hi=300,
+       masks="segment", seg_lookback=1),
+    W_("step_fp32", B=2, Hq=4, Hkv=4, D=64, W=4, dtype="f32", ctx_lo=100, ctx_hi=256),
+]
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("wl", STEP, ids=[w.name for w in STEP])
+def test_verify_step_matches_attention_then_accept_commit(wl, in_place):
+    inp = gpu_inputs(wl, 21)
+    ref_out, ref_lse = oracle_attn(inp)
+    n_ref, path_ref, bonus_ref = oracle_accept(inp)
+    kc_ref, vc_ref, ctx_ref = O.kv_commit(raw(inp["k_cache"]), raw(inp["v_cache"]),
+                                          raw(inp["k_new"]), raw(inp["v_new"]), n_ref, path_ref,
+                                          ints(inp["block_table"]), ints(inp["ctx_lens"]))
+    ctx = inp["ctx_lens"].clone()
+    ctx_out = ctx if in_place else torch.full_like(ctx, -3)
+    out, lse, n, path, bonus, ctx_out = lib.verify_step(
+        inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], ctx, inp["k_new"],
+        inp["v_new"], inp["mask_kind"], inp["mask_ids"], inp["logits"], inp["draft_ids"],
+        ctx_lens_out=ctx_out, max_ctx_len=int(inp["host"]["ctx_lens"].max()), scale=inp["scale"],
+        seg_lookback=inp["seg_lookback"])
+    torch.cuda.synchronize()
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
+    assert_accept_equal((n, path, bonus), (n_ref, path_ref, bonus_ref))
+    assert np.array_equal(ints(ctx_out), ctx_ref)
+    assert np.array_equal(raw(inp["k_cache"]), kc_ref)
+    assert np.array_equal(raw(inp["v_cache"]), vc_ref)
