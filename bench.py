@@ -34,7 +34,8 @@ from speculative_decoding_verify_mtp_amd import lib  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bitnet2b_chain"
-KERNEL_SOURCES = ["attn_mfma.hpp", "attn_valu.hpp", "common.hpp"]
+KERNEL_SOURCES = ["attn_lds.hpp", "attn_mfma.hpp", "attn_stream.hpp", "attn_valu.hpp",
+                  "common.hpp", "mtp_verify.hip"]
 
 
 def kernel_source_hash() -> str:

@@ -210,11 +210,13 @@ mtp_status mtp_accept_commit(const mtp_shape* shape, const float* logits, int32_
 
 /* The whole verify step in two launches: the split-K partial kernel, then
  * one launch that runs the combine (out, lse) side by side with acceptance
- * and commit.  Arguments as for mtp_verify_attn and mtp_accept_commit;
+ * and commit (they do not depend on each other: the combine reads partial
+ * results and ctx_lens_in, the commit writes cache slots >= ctx_len and
+ * ctx_lens_out).  Arguments as for mtp_verify_attn and mtp_accept_commit;
  * attention reads ctx_lens_in and the cache as they are before the commit.
  * When ctx_lens_out aliases ctx_lens_in the combine and the commit run as
- * two launches instead (the combine reads the lengths the commit updates).
- * Results are those of mtp_verify_attn followed by mtp_accept_commit. */
+ * two ordered launches instead.  Results are those of mtp_verify_attn
+ * followed by mtp_accept_commit. */
 mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache, void* v_cache,
                            const int32_t* block_table, const int32_t* ctx_lens_in,
                            const void* k_new, const void* v_new, const uint8_t* mask_kind,

@@ -1,6 +1,6 @@
-// Greedy acceptance and KV commit.  One workgroup (4 waves) per sequence.
+// Greedy acceptance and KV commit.  One workgroup per sequence.
 //
-// Acceptance: the four waves take the block rows in turn and reduce the argmax
+// Acceptance: the waves take the block rows in turn and reduce the argmax
 // of each row's logits (smallest id on ties).  Wave 0 then maps block node i
 // to lane i: match_i = (draft_i >= 0 and draft_i == target[parent_i]); the
 // node is accepted when every node on its root path matches, i.e. when its
@@ -52,7 +52,7 @@ struct Prefetch {
   int kind, id, draft, L, page;
 };
 
-__device__ inline Prefetch prefetch_inputs(const AcceptParams& ap, const CommitParams* cp, int b) {
+__device__ __forceinline__ Prefetch prefetch_inputs(const AcceptParams& ap, const CommitParams* cp, int b) {
   const int lane = threadIdx.x & 63;
   const int W = ap.W;
   Prefetch f;
@@ -70,13 +70,14 @@ __device__ inline Prefetch prefetch_inputs(const AcceptParams& ap, const CommitP
   return f;
 }
 
-// Argmax of every block row into s_tgt[0..W).  All 256 threads take part;
+// Argmax of every block row into s_tgt[0..W).  All waves take part;
 // 16-byte loads when rows are 16-byte aligned (V % 4 == 0).
-__device__ inline void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
+__device__ __forceinline__ void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const bool vec = (p.V & 3) == 0 && ((uintptr_t)p.logits & 15) == 0;
-  for (int i = wv; i < p.W; i += 4) {
+  for (int i = wv; i < p.W; i += nw) {
     const float* row = p.logits + ((size_t)b * p.W + i) * p.V;
     float bv = neg_inf();
     int bi = 0x7fffffff;
@@ -119,7 +120,7 @@ __device__ inline void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
 
 // Acceptance of sequence b by wave 0 (lane = node).  Returns the accepted
 // length (-1 for a malformed mask) and fills s_path[0..len] with the path.
-__device__ inline int wave_accept(const AcceptParams& p, int b, const Prefetch& f, const int* s_tgt,
+__device__ __forceinline__ int wave_accept(const AcceptParams& p, int b, const Prefetch& f, const int* s_tgt,
                                   int* s_path) {
   const int lane = threadIdx.x & 63;
   const int W = p.W;
@@ -173,7 +174,7 @@ __device__ inline int wave_accept(const AcceptParams& p, int b, const Prefetch& 
 // publishes the copy list in LDS; then all threads copy.  When fused, `a` and
 // s_path come from the acceptance; otherwise they are read from memory.
 template <bool kFused>
-__device__ inline void block_commit(const CommitParams& p, int b, const Prefetch& f, int a_fused,
+__device__ __forceinline__ void block_commit(const CommitParams& p, int b, const Prefetch& f, int a_fused,
                                     const int* s_path, int* s_src, int* s_dst, int* s_meta) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < kWave) {
@@ -246,25 +247,105 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
   block_commit<false>(p, b, f, 0, nullptr, s_src, s_dst, s_meta);
 }
 
-// Acceptance then commit of sequence b by one 256-thread workgroup.
-__device__ inline void accept_commit_seq(const AcceptParams& ap, const CommitParams& cp, int b) {
-  __shared__ int s_tgt[MTP_MAX_W];
-  __shared__ int s_path[MTP_MAX_W];
-  __shared__ int s_src[MTP_MAX_W];
-  __shared__ int s_dst[MTP_MAX_W];
-  __shared__ int s_meta[2];
+// LDS scratch of one fused acceptance + commit, in ints.
+constexpr int kAcceptScratchInts = 4 * MTP_MAX_W + 2;
+
+// Acceptance then commit of sequence b by one workgroup (any number of
+// waves; wave 0 does the per-node work).  `sm` is kAcceptScratchInts ints of
+// LDS.  The block's new K/V rows are fetched into registers at the start,
+// beside the logits, when they fit (kPre 16-byte chunks per thread and
+// tensor); the commit is then only stores.
+__device__ __forceinline__ void accept_commit_seq(const AcceptParams& ap, const CommitParams& cp, int b,
+                                         int* sm) {
+  constexpr int kPre = 8;
+  int* s_tgt = sm;
+  int* s_path = sm + MTP_MAX_W;
+  int* s_pos = sm + 2 * MTP_MAX_W;  // path position of a block row, -1 if not committed
+  int* s_dst = sm + 3 * MTP_MAX_W;  // destination slot of a path position
+  int* s_meta = sm + 4 * MTP_MAX_W;
+  const int lane = threadIdx.x & 63;
+  const int chunks = cp.row_bytes >> 4;
+  const int all = ap.W * chunks;
+  const bool pre = all <= kPre * (int)blockDim.x;
+  const char* kn = static_cast<const char*>(cp.k_new);
+  const char* vn = static_cast<const char*>(cp.v_new);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 pk[kPre], pv[kPre];
+  if (pre) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int idx = threadIdx.x + u * blockDim.x;
+      if (idx < all) {
+        const int row = idx / chunks;
+        const size_t src = ((size_t)b * ap.W + row) * cp.row_bytes + (size_t)(idx - row * chunks) * 16;
+        pk[u] = *reinterpret_cast<const u32x4*>(kn + src);
+        pv[u] = *reinterpret_cast<const u32x4*>(vn + src);
+      }
+    }
+  }
   Prefetch f{};
   if (threadIdx.x < kWave) f = prefetch_inputs(ap, &cp, b);
   block_argmax(ap, b, s_tgt);
   __syncthreads();
-  int a = -1;
-  if (threadIdx.x < kWave) a = wave_accept(ap, b, f, s_tgt, s_path);
+  if (threadIdx.x < kWave) {
+    const int a = wave_accept(ap, b, f, s_tgt, s_path);
+    // validate the commit: one path position per lane
+    const int L = f.L;
+    const int first = cp.skip_root ? 1 : 0;
+    const bool a_ok = a >= 0 && a <= ap.W - 1 && L >= 0;
+    bool bad_k = false;
+    int row = -1;
+    if (a_ok && lane >= first && lane <= a) {
+      row = s_path[lane];
+      bad_k = row < 0 || row >= ap.W || f.page < 0 || f.page >= cp.num_pages;
+      s_dst[lane] = f.page * kPage + ((L + lane) & 15);
+    }
+    const bool good = a_ok && __ballot(bad_k) == 0ull;
+    if (lane < ap.W) s_pos[lane] = -1;
+    if (good && row >= 0) s_pos[row] = lane;  // after the reset: LDS writes of a wave stay in order
+    if (lane == 0) {
+      s_meta[0] = good ? a : -1;
+      s_meta[1] = first;
+      cp.ctx_out[b] = good ? L + a + 1 : L;  // L was read before any write of ctx_out
+      if (!good) raise_status(a_ok ? MTP_DEV_BAD_PAGE : MTP_DEV_BAD_ACCEPT);
+    }
+  }
   __syncthreads();
-  block_commit<true>(cp, b, f, a, s_path, s_src, s_dst, s_meta);
+  const int a = s_meta[0];
+  const int first = s_meta[1];
+  if (a < first) return;
+  char* kc = static_cast<char*>(cp.k_cache);
+  char* vc = static_cast<char*>(cp.v_cache);
+  if (pre) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int idx = threadIdx.x + u * blockDim.x;
+      if (idx < all) {
+        const int row = idx / chunks;
+        const int k = s_pos[row];
+        if (k >= 0) {
+          const size_t dst = (size_t)s_dst[k] * cp.row_bytes + (size_t)(idx - row * chunks) * 16;
+          *reinterpret_cast<u32x4*>(kc + dst) = pk[u];
+          *reinterpret_cast<u32x4*>(vc + dst) = pv[u];
+        }
+      }
+    }
+  } else {
+    const int total = (a - first + 1) * chunks;
+    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+      const int k = first + idx / chunks;
+      const size_t ch = (size_t)(idx % chunks) * 16;
+      const size_t src = ((size_t)b * ap.W + s_path[k]) * cp.row_bytes + ch;
+      const size_t dst = (size_t)s_dst[k] * cp.row_bytes + ch;
+      *reinterpret_cast<uint4*>(kc + dst) = *reinterpret_cast<const uint4*>(kn + src);
+      *reinterpret_cast<uint4*>(vc + dst) = *reinterpret_cast<const uint4*>(vn + src);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptParams ap, CommitParams cp) {
-  accept_commit_seq(ap, cp, blockIdx.x);
+  __shared__ int sm[kAcceptScratchInts];
+  accept_commit_seq(ap, cp, blockIdx.x, sm);
 }
 
 }  // namespace mtpv

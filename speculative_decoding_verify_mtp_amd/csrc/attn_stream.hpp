@@ -54,6 +54,8 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
   __shared__ __attribute__((aligned(16))) char ring[NS * kStageBytes];
   __shared__ int s_pref[kStreamMaxB + 1];
 
+  const int wg = (int)blockIdx.x;  // this workgroup's range index
+  const int G = (int)gridDim.x;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int c = lane & 15;
@@ -82,8 +84,8 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
   }
   __syncthreads();
   const int total = s_pref[p.B];
-  const int T = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-  int g = (int)blockIdx.x * T;
+  const int T = (total + G - 1) / G;
+  int g = wg * T;
   const int g_end = min(g + T, total);
   if (g >= g_end) return;  // uniform over the workgroup
 
@@ -152,8 +154,8 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
         vrow[k] = 0;
       }
       if (i0 == 0 && threadIdx.x == 0) {
-        sp.seg_info[2 * sigma] = (int)blockIdx.x + sigma;
-        sp.seg_info[2 * sigma + 1] = (seg_end_g - 1) / T - (int)blockIdx.x + 1;
+        sp.seg_info[2 * sigma] = wg + sigma;
+        sp.seg_info[2 * sigma + 1] = (seg_end_g - 1) / T - wg + 1;
       }
     }
 
@@ -298,7 +300,7 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
           for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{qnan(), qnan(), qnan(), qnan()};
         }
       }
-      const size_t piece = (size_t)blockIdx.x + sigma;
+      const size_t piece = (size_t)wg + sigma;
 #pragma unroll
       for (int k = 0; k < RB; ++k) {
         float l = st.l[k];

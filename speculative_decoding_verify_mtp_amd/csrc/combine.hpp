@@ -20,7 +20,7 @@ namespace mtpv {
 // kStream = true : pieces of the stream kernel, [pieces, rows_block] rows,
 //                  located through the segment table.
 template <int D, bool kStream>
-__device__ inline void combine_rows(const AttnParams& p, const StreamParams& sp, unsigned block) {
+__device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamParams& sp, unsigned block) {
   constexpr int VPL = D / 16;  // accumulators per lane per split
   const int lane = threadIdx.x & 63;
   const int gq = lane >> 4, gl = lane & 15;
@@ -202,10 +202,11 @@ __global__ __launch_bounds__(256) void attn_combine(AttnParams p, StreamParams s
 template <int D, bool kStream>
 __global__ __launch_bounds__(256) void finish_kernel(AttnParams p, StreamParams sp, AcceptParams ap,
                                                      CommitParams cp, unsigned combine_blocks) {
+  __shared__ int sm[kAcceptScratchInts];
   if (blockIdx.x < combine_blocks)
     combine_rows<D, kStream>(p, sp, blockIdx.x);
   else
-    accept_commit_seq(ap, cp, (int)(blockIdx.x - combine_blocks));
+    accept_commit_seq(ap, cp, (int)(blockIdx.x - combine_blocks), sm);
 }
 
 }  // namespace mtpv

@@ -66,7 +66,7 @@ __device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
 //  SEGMENT : own-segment rows up to i, plus rows of the `lookback` previous
 //            segments (all earlier segments when lookback < 0).
 // `id` is this lane's mask id (ids[lane] for lane < W, anything otherwise).
-__device__ inline uint64_t node_visibility(int kind, int id, int W, int lookback, int lane,
+__device__ __forceinline__ uint64_t node_visibility(int kind, int id, int W, int lookback, int lane,
                                            bool& ok) {
   const bool in = lane < W;
   if (!in) id = 0;
