@@ -45,6 +45,11 @@ What it computes, step by step, in the notation of the pages:
   left-to-right acceptance); ties go to the smaller node index.  The bonus
   (verifier-origin) token is the target at the accepted node (BitMTP §3.3).
 
+* Hybrid acceptance (``accept_hybrid``).  The drafter's probability of each
+  drafted token decides a confidence prefix h; h >= m commits the h drafts
+  without the verifier, otherwise the greedy verification above decides
+  (BitMTP §3.3 hybrid decoding; Multi-Byte Prediction §3.1 byte acceptance).
+
 * Commit (``kv_commit``).  The K/V rows of the accepted path, root first, are
   copied to logical positions L, L+1, ..., L+a; rejected rows are never
   written and the KV boundary advances by a+1 (BitMTP §3.4 M2: accepted draft
@@ -291,3 +296,83 @@ def kv_commit(k_cache, v_cache, k_new, v_new, accept_len, accept_path, block_tab
             vc[page, slot] = v_new[b, row]
         ctx[b] = L + a + 1
     return kc, vc, ctx
+
+
+# ----------------------------------------------------------------------------
+# confidence-threshold and hybrid acceptance
+# ----------------------------------------------------------------------------
+
+def draft_confidence(draft_logits, draft_ids):
+    """[B, W] fp64: the drafter's softmax probability of each drafted token
+    (row i of draft_logits is the distribution that produced draft i;
+    "Dynamic Multi-Byte Prediction With Hierarchical Language Models" Sec. 3.1:
+    a predicted byte is accepted when the model's probability for it reaches
+    the threshold).  Mask tokens (draft < 0) and row 0 get confidence 0."""
+    x = np.asarray(draft_logits, dtype=np.float64)
+    B, W, V = x.shape
+    conf = np.zeros((B, W))
+    for b in range(B):
+        for i in range(1, W):
+            d = int(draft_ids[b, i])
+            if d < 0 or d >= V:
+                continue
+            row = x[b, i]
+            m = row.max()
+            e = np.exp(row - m)
+            conf[b, i] = e[d] / e.sum()
+    return conf
+
+
+def accept_hybrid(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau, min_prefix):
+    """Hybrid acceptance ("BitMTP: When Multi-Token Prediction Meets Low-Bit
+    Large Language Models", Sec. 3.3): the confidence prefix h is the number of
+    leading drafts whose confidence reaches tau (a tree takes the deepest root
+    path of confident nodes, smallest index on ties; Sec. 3.1 of the
+    multi-byte page: left to right, the first below the threshold and
+    everything after it discarded).  If h >= min_prefix the h draft tokens are
+    committed without the verifier: the step emits h tokens, the last of which
+    becomes the next anchor, so accept_len = h - 1 (drafts committed besides
+    the anchor), the path is the root path of the h-th token's parent and the
+    bonus is the h-th draft token.  Otherwise the greedy verification result
+    (``accept``) is used; ``logits`` may be None, and then those sequences get
+    -1 outputs.  Returns accept_len, accept_path, bonus_id, conf_len (h)."""
+    draft_logits = np.asarray(draft_logits)
+    B, W = draft_logits.shape[0], draft_logits.shape[1]
+    conf = draft_confidence(draft_logits, draft_ids)
+    if logits is not None:
+        v_len, v_path, v_bonus = accept(logits, draft_ids, mask_kind, mask_ids)
+    acc_len = np.full(B, -1, dtype=np.int64)
+    path = np.full((B, W), -1, dtype=np.int64)
+    bonus = np.full(B, -1, dtype=np.int64)
+    conf_len = np.full(B, -1, dtype=np.int64)
+    for b in range(B):
+        kind, ids = int(mask_kind[b]), np.asarray(mask_ids[b])
+        if not mask_is_valid(kind, ids):
+            continue
+        par = acceptance_parents(kind, ids)
+        ok = np.zeros(W, dtype=bool)
+        depth = np.zeros(W, dtype=np.int64)
+        ok[0] = True
+        for i in range(1, W):
+            p = int(par[i])
+            depth[i] = depth[p] + 1
+            ok[i] = ok[p] and conf[b, i] >= tau
+        best = 0
+        for i in range(1, W):
+            if ok[i] and depth[i] > depth[best]:
+                best = i
+        h = int(depth[best])
+        conf_len[b] = h
+        if h >= min_prefix and h >= 1:
+            chain = []
+            j = int(par[best])
+            while j >= 0:
+                chain.append(j)
+                j = int(par[j])
+            chain.reverse()
+            acc_len[b] = h - 1
+            path[b, :len(chain)] = chain
+            bonus[b] = int(draft_ids[b, best])
+        elif logits is not None:
+            acc_len[b], path[b], bonus[b] = v_len[b], v_path[b], v_bonus[b]
+    return acc_len, path, bonus, conf_len

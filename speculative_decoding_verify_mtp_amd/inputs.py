@@ -25,7 +25,13 @@ Recipe (all drawn from one seed):
   * a drafted child of node p equals target[p] with probability ``match_p``
     (first child; if it misses, one other child matches with probability
     1/2); other siblings get distinct non-matching ids, so the accepted path
-    is unique.
+    is unique;
+  * drafter logits (for confidence acceptance): N(0, 0.1^2) per entry, with
+    the drafted token's logit set to a "lift" drawn from CONFIDENT_LIFTS with
+    probability ``conf_p``, else from DOUBTFUL_LIFTS.  With a 1000-token
+    vocabulary the drafted token's probability is then about 0.96/0.99/0.999
+    or 0.05/0.29/0.75: at least 0.04 away from a 0.9 threshold.  Drawn after
+    every other input, so the other inputs do not depend on these.
 """
 from __future__ import annotations
 
@@ -37,6 +43,10 @@ import torch
 
 PAGE_SIZE = 16
 MASK_CHAIN, MASK_TREE, MASK_SEGMENT = 0, 1, 2
+
+
+CONFIDENT_LIFTS = (10.0, 12.0, 14.0)
+DOUBTFUL_LIFTS = (4.0, 6.0, 8.0)
 
 
 @dataclass(frozen=True)
@@ -61,6 +71,7 @@ class Workload:
     spare_pages: int = 64
     vocab: int = 1000
     mask_token_rows: int = 0  # trailing rows whose draft id is -1 (never accepted)
+    conf_p: float = 0.8  # probability that a draft's logit lift is a confident one
 
     @property
     def group(self) -> int:
@@ -209,8 +220,13 @@ def make_structure(wl: Workload, seed: int) -> dict:
     tgt = rng.integers(0, wl.vocab, size=(B, W)).astype(np.int32)
     draft = np.stack([draw_drafts(rng, accept_parent[b], tgt[b], wl.vocab, wl.match_p,
                                   wl.mask_token_rows) for b in range(B)])
+    confident = rng.random((B, W)) < wl.conf_p
+    lift = np.where(confident, rng.choice(CONFIDENT_LIFTS, size=(B, W)),
+                    rng.choice(DOUBTFUL_LIFTS, size=(B, W))).astype(np.float32)
+    lift_tok = np.where(draft >= 0, draft, rng.integers(0, wl.vocab, size=(B, W))).astype(np.int32)
     return dict(ctx_lens=ctx, mask_kind=kinds, mask_ids=ids, block_table=table,
-                num_pages=pool, target_ids=tgt, draft_ids=draft)
+                num_pages=pool, target_ids=tgt, draft_ids=draft, draft_lift=lift,
+                draft_lift_token=lift_tok)
 
 
 def valid_slots(block_table: np.ndarray, ctx_lens: np.ndarray, num_pages: int) -> np.ndarray:
@@ -265,6 +281,11 @@ def make_inputs(wl: Workload, seed: int, device: str | torch.device = "cpu",
     tgt = torch.from_numpy(st["target_ids"]).to(device=device, dtype=torch.int64)
     lift = logits.amax(dim=-1, keepdim=True) + 1.0
     logits.scatter_(-1, tgt.unsqueeze(-1), lift)
+    draft_logits = 0.1 * torch.randn((B, W, wl.vocab), generator=gen, device=device,
+                                     dtype=torch.float32)
+    lt = torch.from_numpy(st["draft_lift_token"]).to(device=device, dtype=torch.int64)
+    draft_logits.scatter_(-1, lt.unsqueeze(-1),
+                          torch.from_numpy(st["draft_lift"]).to(device).unsqueeze(-1))
     if poison:
         valid = torch.from_numpy(valid_slots(st["block_table"], st["ctx_lens"], npages))
         invalid = (~valid).to(device)
@@ -279,7 +300,7 @@ def make_inputs(wl: Workload, seed: int, device: str | torch.device = "cpu",
         q=q, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
         block_table=it(st["block_table"]), ctx_lens=it(st["ctx_lens"]),
         mask_kind=it(st["mask_kind"], torch.uint8), mask_ids=it(st["mask_ids"]),
-        logits=logits, draft_ids=it(st["draft_ids"]),
+        logits=logits, draft_ids=it(st["draft_ids"]), draft_logits=draft_logits,
         seg_lookback=wl.seg_lookback, scale=1.0 / math.sqrt(D),
     )
 

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import verify_oracle as O
+from tests import test_oracle_hybrid as H
 from tests import test_oracle_pins as P
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -88,6 +89,31 @@ def _page_slot_swapped(block_row, t):
     return int(block_row[t // O.PAGE]), (t + 1) % O.PAGE
 
 
+def _confidence_of_previous_row(draft_logits, draft_ids, _orig=O.draft_confidence):
+    x = np.asarray(draft_logits)
+    return _orig(np.concatenate([x[:, :1], x[:, :-1]], axis=1), draft_ids)
+
+
+def _confidence_is_max_probability(draft_logits, draft_ids, _orig=O.draft_confidence):
+    x = np.asarray(draft_logits)
+    top = np.argmax(x, axis=-1)
+    top[np.asarray(draft_ids) < 0] = -1
+    return _orig(x, top)
+
+
+def _hybrid_commits_h_drafts(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau,
+                             min_prefix, _orig=O.accept_hybrid):
+    n, path, bonus, h = _orig(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau,
+                              min_prefix)
+    hit = (h >= min_prefix) & (h >= 1)
+    return np.where(hit, h, n), path, bonus, h
+
+
+def _hybrid_strict_min_prefix(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau,
+                              min_prefix, _orig=O.accept_hybrid):
+    return _orig(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau, min_prefix + 1)
+
+
 MUTANTS = [
     ("block_visibility", _tree_vis_without_self, [(P.test_tree_visibility_is_ancestor_closure, 3),
                                                   (P.test_tree_golden_fixture,)]),
@@ -101,6 +127,13 @@ MUTANTS = [
     ("target_ids", _targets_argmin, [(P.test_accept_golden_tree,)]),
     ("target_ids", _targets_last_on_ties, [(P.test_argmax_ties_take_the_smallest_id,)]),
     ("page_slot", _page_slot_swapped, [(P.test_commit_writes_exactly_the_accepted_rows, False)]),
+    ("draft_confidence", _confidence_of_previous_row,
+     [(H.test_confidence_is_the_softmax_probability_of_the_drafted_token,), (H.test_hybrid_golden_chain,)]),
+    ("draft_confidence", _confidence_is_max_probability,
+     [(H.test_confidence_is_the_softmax_probability_of_the_drafted_token,)]),
+    ("accept_hybrid", _hybrid_commits_h_drafts, [(H.test_hybrid_golden_chain,),
+                                                 (H.test_chain_confidence_prefix_closed_form, 0)]),
+    ("accept_hybrid", _hybrid_strict_min_prefix, [(H.test_hybrid_golden_chain,)]),
 ]
 
 
