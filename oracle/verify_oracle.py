@@ -326,7 +326,7 @@ def draft_confidence(draft_logits, draft_ids):
 def accept_hybrid(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau, min_prefix):
     """Hybrid acceptance ("BitMTP: When Multi-Token Prediction Meets Low-Bit
     Large Language Models", Sec. 3.3): the confidence prefix h is the number of
-    leading drafts whose confidence reaches tau (a tree takes the deepest root
+    leading drafts whose confidence reaches tau (mask tokens never count; a tree takes the deepest root
     path of confident nodes, smallest index on ties; Sec. 3.1 of the
     multi-byte page: left to right, the first below the threshold and
     everything after it discarded).  If h >= min_prefix the h draft tokens are
@@ -356,7 +356,8 @@ def accept_hybrid(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau, min
         for i in range(1, W):
             p = int(par[i])
             depth[i] = depth[p] + 1
-            ok[i] = ok[p] and conf[b, i] >= tau
+            token = 0 <= int(draft_ids[b, i]) < draft_logits.shape[2]
+            ok[i] = ok[p] and token and conf[b, i] >= tau
         best = 0
         for i in range(1, W):
             if ok[i] and depth[i] > depth[best]:

@@ -27,11 +27,13 @@ Recipe (all drawn from one seed):
     1/2); other siblings get distinct non-matching ids, so the accepted path
     is unique;
   * drafter logits (for confidence acceptance): N(0, 0.1^2) per entry, with
-    the drafted token's logit set to a "lift" drawn from CONFIDENT_LIFTS with
-    probability ``conf_p``, else from DOUBTFUL_LIFTS.  With a 1000-token
-    vocabulary the drafted token's probability is then about 0.96/0.99/0.999
-    or 0.05/0.29/0.75: at least 0.04 away from a 0.9 threshold.  Drawn after
-    every other input, so the other inputs do not depend on these.
+    the drafted token's logit set to log(p / (1 - p)) + log(vocab - 1), where
+    the intended probability p is drawn from CONFIDENT_PROBS with probability
+    ``conf_p``, else from DOUBTFUL_PROBS; the drafted token's softmax
+    probability is then p up to the noise of the other entries (a few
+    thousandths of the odds), so with 7 or more tokens every confidence
+    stays at least 0.04 away from a 0.9 threshold.  Drawn after every other input, so the other
+    inputs do not depend on these.
 """
 from __future__ import annotations
 
@@ -45,8 +47,8 @@ PAGE_SIZE = 16
 MASK_CHAIN, MASK_TREE, MASK_SEGMENT = 0, 1, 2
 
 
-CONFIDENT_LIFTS = (10.0, 12.0, 14.0)
-DOUBTFUL_LIFTS = (4.0, 6.0, 8.0)
+CONFIDENT_PROBS = (0.95, 0.99, 0.999)
+DOUBTFUL_PROBS = (0.05, 0.3, 0.75)
 
 
 @dataclass(frozen=True)
@@ -221,8 +223,9 @@ def make_structure(wl: Workload, seed: int) -> dict:
     draft = np.stack([draw_drafts(rng, accept_parent[b], tgt[b], wl.vocab, wl.match_p,
                                   wl.mask_token_rows) for b in range(B)])
     confident = rng.random((B, W)) < wl.conf_p
-    lift = np.where(confident, rng.choice(CONFIDENT_LIFTS, size=(B, W)),
-                    rng.choice(DOUBTFUL_LIFTS, size=(B, W))).astype(np.float32)
+    p = np.where(confident, rng.choice(CONFIDENT_PROBS, size=(B, W)),
+                 rng.choice(DOUBTFUL_PROBS, size=(B, W)))
+    lift = (np.log(p / (1 - p)) + math.log(max(wl.vocab - 1, 1))).astype(np.float32)
     lift_tok = np.where(draft >= 0, draft, rng.integers(0, wl.vocab, size=(B, W))).astype(np.int32)
     return dict(ctx_lens=ctx, mask_kind=kinds, mask_ids=ids, block_table=table,
                 num_pages=pool, target_ids=tgt, draft_ids=draft, draft_lift=lift,

@@ -141,18 +141,22 @@ def test_threshold_above_one_always_verifies():
     assert np.array_equal(n, g[0]) and np.array_equal(path, g[1]) and np.array_equal(bonus, g[2])
 
 
-def test_mask_tokens_are_never_confident():
+@pytest.mark.parametrize("tau", [0.9, 0.0, -1.0])
+def test_mask_tokens_are_never_confident(tau):
     wl = _wl(masks="chain", B=4, W=10, conf_p=1.0, mask_token_rows=4)
     inp = I.make_inputs(wl, 2)
     st = inp["host"]
     _, _, _, h = O.accept_hybrid(inp["draft_logits"].numpy(), None, st["draft_ids"],
-                                 st["mask_kind"], st["mask_ids"], 0.9, 1)
+                                 st["mask_kind"], st["mask_ids"], tau, 1)
     assert np.all(h == 5)
 
 
-def test_generator_keeps_confidences_away_from_the_threshold():
-    wl = _wl(masks="mixed", B=40, W=16, conf_p=0.5)
+@pytest.mark.parametrize("vocab,masks", [(7, "mixed"), (1000, "mixed"), (50000, "chain")])
+def test_generator_keeps_confidences_away_from_the_threshold(vocab, masks):
+    wl = _wl(masks=masks, B=40, W=16, conf_p=0.5, vocab=vocab)
     inp = I.make_inputs(wl, 9)
-    c = O.draft_confidence(inp["draft_logits"].numpy(), inp["host"]["draft_ids"])
-    live = c[:, 1:][inp["host"]["draft_ids"][:, 1:] >= 0]
+    c = softmax(inp["draft_logits"].numpy().astype(np.float64), axis=-1)
+    d = inp["host"]["draft_ids"]
+    live = np.array([c[b, i, d[b, i]] for b in range(wl.B) for i in range(1, wl.W) if d[b, i] >= 0])
+    assert live.size > 100
     assert np.all(np.abs(live - 0.9) > 0.04)
