@@ -110,6 +110,75 @@ def cpu_baseline(wl: I.Workload, seed: int, budget_s: float) -> dict:
                       f"(ctx {host['ctx_lens'].tolist()}) in {dt:.1f} s, fp64 numpy"}
 
 
+def timed_graph(launch, steps: int, warmup: int) -> float:
+    """Milliseconds per launch of `launch()`, from HIP events around replays of
+    a graph that holds 100 launches."""
+    launch()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    n = 100
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(n):
+                launch()
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup // n)):
+        g.replay()
+    reps = max(1, steps // n)
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    z.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(z) / (reps * n)
+
+
+def bench_accept_hybrid(wl: I.Workload, inp: dict, args) -> int:
+    """Confidence / hybrid acceptance on its own: one launch per step over the
+    batch, with the verifier logits (hybrid) and without (confidence only).
+    Algorithmic bytes: the logits rows read (W - 1 drafter rows, plus W
+    verifier rows when given) and the int32 inputs and outputs."""
+    B, W, V = inp["draft_logits"].shape
+    out = [torch.empty(B, dtype=torch.int32, device="cuda"),
+           torch.empty((B, W), dtype=torch.int32, device="cuda"),
+           torch.empty(B, dtype=torch.int32, device="cuda"),
+           torch.empty(B, dtype=torch.int32, device="cuda")]
+    res = {}
+    for name, logits in (("hybrid", inp["logits"]), ("confidence_only", None)):
+        def launch(logits=logits):
+            lib.accept_hybrid(inp["draft_logits"], logits, inp["draft_ids"], inp["mask_kind"],
+                              inp["mask_ids"], args.tau, args.min_prefix, accept_len=out[0],
+                              accept_path=out[1], bonus_id=out[2], conf_len=out[3])
+        ms = timed_graph(launch, args.steps, args.warmup)
+        rows = (W - 1) + (W if logits is not None else 0)
+        nbytes = B * (rows * V * 4 + W * 4 * 3 + 1 + 4 * 3)
+        res[name] = {"us": round(ms * 1e3, 3), "bytes": nbytes,
+                     "GBs": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+    if lib.device_status(clear=True) != 0:
+        print("bench.py: the device reported a data error", file=sys.stderr)
+        return 3
+    h = res["hybrid"]
+    rec = {
+        "metric": "hybrid acceptance launches/s at 1 GPU (confidence prefix + greedy fallback)",
+        "value": round(1e6 / h["us"], 1), "unit": "launches/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["us"] / 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded drafter and verifier logits)",
+        "config": {"workload": wl.name, "B": B, "W": W, "V": V, "tau": args.tau,
+                   "min_prefix": args.min_prefix},
+        "roofline": {"bound": "hbm", "achieved": h["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(h["GBs"] / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "accept_hybrid_kernel", "kernel_us": h["us"],
+                     "algorithmic_bytes": h["bytes"]},
+        "confidence_only": res["confidence_only"],
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +194,11 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only time a plain device copy of MB megabytes (HBM reference and "
                          "the FETCH_SIZE/WRITE_SIZE calibration kernel), then exit")
+    ap.add_argument("--kernel", default="step", choices=["step", "accept_hybrid"],
+                    help="step: the whole verify step (default); accept_hybrid: only the "
+                         "confidence/hybrid acceptance kernel, timed on its own")
+    ap.add_argument("--tau", type=float, default=0.9)
+    ap.add_argument("--min-prefix", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -166,6 +240,8 @@ def main() -> int:
         wl = wl.scaled(seg_lookback=args.seg_lookback)
     seed = I.workload_seed(args.workload)
     inp = I.make_inputs(wl, seed, device=dev)
+    if args.kernel == "accept_hybrid":
+        return bench_accept_hybrid(wl, inp, args)
     host = inp["host"]
     ctx = host["ctx_lens"]
     nbytes = algorithmic_bytes(wl, ctx)

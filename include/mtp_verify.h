@@ -182,6 +182,35 @@ mtp_status mtp_accept(const mtp_shape* shape, const float* logits, int32_t V,
                       const int32_t* mask_ids, int32_t* accept_len, int32_t* accept_path,
                       int32_t* bonus_id, void* stream);
 
+/* Confidence-threshold and hybrid acceptance ("BitMTP: When Multi-Token
+ * Prediction Meets Low-Bit Large Language Models", Sec. 3.3, with the
+ * threshold rule of "Dynamic Multi-Byte Prediction With Hierarchical
+ * Language Models", Sec. 3.1).  Uses B and W of `shape` only.
+ *
+ *   draft_logits [B, W, V] fp32: row i is the drafter's distribution that
+ *                produced draft i (row 0 unused)
+ *   logits       [B, W, V] fp32 or NULL: the verifier's logits (as for
+ *                mtp_accept); NULL when the verifier has not run
+ *   tau          confidence threshold (NaN rejected); min_prefix = m
+ *   conf_len     [B] int32 (written): confidence prefix h
+ *   other arguments and outputs as for mtp_accept.
+ *
+ * A draft is confident when it is a token (0 <= id < V) and its softmax
+ * probability under draft_logits reaches tau (fp32 arithmetic).  h is the
+ * depth of the deepest node whose whole root path is confident (chains: the
+ * number of leading confident drafts), smallest index on ties.  When h >= 1
+ * and h >= m the h drafts are taken without the verifier: accept_len = h - 1,
+ * accept_path = root path of the deepest confident node's parent, bonus_id =
+ * that node's draft (the next anchor).  Otherwise the outputs are those of
+ * mtp_accept, or -1 (accept_len, bonus_id, whole path) when logits is NULL.
+ * A malformed mask writes -1 to all four outputs.  The outputs feed
+ * mtp_kv_commit unchanged. */
+mtp_status mtp_accept_hybrid(const mtp_shape* shape, const float* draft_logits,
+                             const float* logits, int32_t V, const int32_t* draft_ids,
+                             const uint8_t* mask_kind, const int32_t* mask_ids, float tau,
+                             int32_t min_prefix, int32_t* accept_len, int32_t* accept_path,
+                             int32_t* bonus_id, int32_t* conf_len, void* stream);
+
 /* KV commit.  For path position k = (skip_root ? 1 : 0) .. accept_len[b],
  * copies the bytes of k_new/v_new[b, accept_path[b][k], :, :] to logical
  * position ctx_lens_in[b] + k of k_cache/v_cache, then writes

@@ -10,7 +10,7 @@
 // i writes itself to path position popcount(bits below i).
 //
 // Commit: lanes of wave 0 validate one path position each (row index, page
-// mapping); then all 256 threads copy the accepted rows in 16-byte chunks.  A
+// mapping); then all threads copy the accepted rows in 16-byte chunks.  A
 // K/V row of one token is Hkv * D contiguous elements both in k_new and in a
 // cache slot, so each accepted position is one contiguous copy.
 #pragma once
@@ -70,52 +70,189 @@ __device__ __forceinline__ Prefetch prefetch_inputs(const AcceptParams& ap, cons
   return f;
 }
 
-// Argmax of every block row into s_tgt[0..W).  All waves take part;
-// 16-byte loads when rows are 16-byte aligned (V % 4 == 0).
+// Argmax of one logits row by one wave (smallest id on ties); 16-byte
+// loads when `vec` (V % 4 == 0 and a 16-byte aligned base).
+__device__ __forceinline__ int wave_row_argmax(const float* row, int V, bool vec) {
+  const int lane = threadIdx.x & 63;
+  float bv = neg_inf();
+  int bi = 0x7fffffff;
+  if (vec) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    const int n4 = V >> 2;
+#pragma unroll 4
+    for (int v = lane; v < n4; v += kWave) {
+      const float4 x = r4[v];
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (xs[e] > bv || bi == 0x7fffffff) {
+          bv = xs[e];
+          bi = 4 * v + e;
+        }
+      }
+    }
+  } else {
+    for (int v = lane; v < V; v += kWave) {
+      const float x = row[v];
+      if (x > bv || bi == 0x7fffffff) {
+        bv = x;
+        bi = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  return bi;
+}
+
+__device__ __forceinline__ bool rows_vec(const float* base, int V) {
+  return (V & 3) == 0 && ((uintptr_t)base & 15) == 0;
+}
+
+// Rows of at most kRegV floats (16-byte aligned, V % 4 == 0) are reduced from
+// registers: a wave first issues the loads of up to kRegRows rows (lane l
+// holds the float4 chunks l, l + 64, ...), then reduces them one by one, so
+// that the load latency is paid once per pass instead of once per row.
+constexpr int kRegVec4 = 4;
+constexpr int kRegV = kWave * 4 * kRegVec4;
+constexpr int kRegRows = 2;
+
+// Threads of the acceptance workgroups: 16 waves, so that one register pass
+// (16 x kRegRows rows) covers blocks of up to 32 rows.
+constexpr int kAcceptThreads = 1024;
+
+struct RegRow {
+  float4 x[kRegVec4];
+};
+
+__device__ __forceinline__ void load_reg_row(const float* row, int V, RegRow& r) {
+  const int lane = threadIdx.x & 63;
+  const float4* r4 = reinterpret_cast<const float4*>(row);
+#pragma unroll
+  for (int u = 0; u < kRegVec4; ++u) {
+    const int v = lane + u * kWave;
+    if (v < (V >> 2)) r.x[u] = r4[v];
+  }
+}
+
+// Argmax of a row held by load_reg_row (smallest id on ties).
+__device__ __forceinline__ int reg_row_argmax(const RegRow& r, int V) {
+  const int lane = threadIdx.x & 63;
+  float bv = neg_inf();
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int u = 0; u < kRegVec4; ++u) {
+    const int v = lane + u * kWave;
+    if (v < (V >> 2)) {
+      const float xs[4] = {r.x[u].x, r.x[u].y, r.x[u].z, r.x[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (xs[e] > bv || bi == 0x7fffffff) {
+          bv = xs[e];
+          bi = 4 * v + e;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  return bi;
+}
+
+// Argmax of every block row into s_tgt[0..W).  All waves take part, row i
+// on wave i % waves.
 __device__ __forceinline__ void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  const bool vec = (p.V & 3) == 0 && ((uintptr_t)p.logits & 15) == 0;
+  const bool vec = rows_vec(p.logits, p.V);
+  const float* base = p.logits + (size_t)b * p.W * p.V;
+  if (vec && p.V <= kRegV) {
+    for (int i0 = wv; i0 < p.W; i0 += nw * kRegRows) {
+      RegRow rr[kRegRows];
+#pragma unroll
+      for (int r = 0; r < kRegRows; ++r) {
+        const int i = i0 + r * nw;
+        if (i < p.W) load_reg_row(base + (size_t)i * p.V, p.V, rr[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < kRegRows; ++r) {
+        const int i = i0 + r * nw;
+        if (i < p.W) {
+          const int bi = reg_row_argmax(rr[r], p.V);
+          if (lane == 0) s_tgt[i] = bi;
+        }
+      }
+    }
+    return;
+  }
   for (int i = wv; i < p.W; i += nw) {
-    const float* row = p.logits + ((size_t)b * p.W + i) * p.V;
-    float bv = neg_inf();
-    int bi = 0x7fffffff;
-    if (vec) {
-      const float4* r4 = reinterpret_cast<const float4*>(row);
-      const int n4 = p.V >> 2;
-#pragma unroll 4
-      for (int v = lane; v < n4; v += kWave) {
-        const float4 x = r4[v];
-        const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (xs[e] > bv || bi == 0x7fffffff) {
-            bv = xs[e];
-            bi = 4 * v + e;
-          }
-        }
-      }
-    } else {
-      for (int v = lane; v < p.V; v += kWave) {
-        const float x = row[v];
-        if (x > bv || bi == 0x7fffffff) {
-          bv = x;
-          bi = v;
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    const int bi = wave_row_argmax(base + (size_t)i * p.V, p.V, vec);
     if (lane == 0) s_tgt[i] = bi;
   }
+}
+
+// Acceptance structure of block node `lane` (wave 0, lane = node): its
+// ancestor-or-self bit row and its parent (0 for the root and for lanes past
+// the block).  CHAIN and SEGMENT blocks accept by index order, TREE blocks
+// along parent pointers.  `ok` is false for a malformed mask description.
+struct NodeTree {
+  uint64_t anc;
+  int par;
+  bool ok;
+};
+
+__device__ __forceinline__ NodeTree node_tree(int kind, int id, int W) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < W;
+  NodeTree t;
+  if (kind == MTP_MASK_TREE) {
+    t.anc = node_visibility(kind, id, W, -1, lane, t.ok);
+    t.par = (in && lane >= 1 && t.ok) ? id : 0;
+  } else {
+    node_visibility(kind, id, W, -1, lane, t.ok);  // validates the description
+    t.anc = in ? (~0ull >> (63 - lane)) : 0ull;
+    t.par = lane >= 1 ? lane - 1 : 0;
+  }
+  return t;
+}
+
+// Deepest node whose whole root path is in `good_bits` (bit 0, the root, is
+// always taken), smallest index on ties, packed as depth * 64 + (63 - node).
+__device__ __forceinline__ int deepest_good(uint64_t good_bits, const NodeTree& t, int W) {
+  const int lane = threadIdx.x & 63;
+  const bool good = lane < W && (t.anc & ~(good_bits | 1ull)) == 0ull;
+  return wave_max_int(good ? (__popcll(t.anc) - 1) * 64 + (63 - lane) : -1);
+}
+
+// Writes the nodes of bit row `ab` (a root path) to path[0..len], root
+// first, and -1 to path[len+1..W).  Path nodes write themselves to their
+// depth; positions past len are padded by the lane of the same index (a
+// different address even when that lane is itself a path node: its depth is
+// <= len < lane).
+__device__ __forceinline__ void write_path(uint64_t ab, int len, int W, int32_t* path, int* s_path) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < W;
+  if (in && ((ab >> lane) & 1ull)) {
+    const int pos = __popcll(ab & ((1ull << lane) - 1ull));
+    path[pos] = lane;
+    if (s_path != nullptr) s_path[pos] = lane;
+  }
+  if (in && lane > len) path[lane] = -1;
 }
 
 // Acceptance of sequence b by wave 0 (lane = node).  Returns the accepted
@@ -125,19 +262,9 @@ __device__ __forceinline__ int wave_accept(const AcceptParams& p, int b, const P
   const int lane = threadIdx.x & 63;
   const int W = p.W;
   const bool in = lane < W;
-  bool ok;
-  uint64_t anc;
-  int par;
-  if (f.kind == MTP_MASK_TREE) {
-    anc = node_visibility(f.kind, f.id, W, -1, lane, ok);
-    par = (in && lane >= 1 && ok) ? f.id : 0;
-  } else {
-    node_visibility(f.kind, f.id, W, -1, lane, ok);  // validates the description
-    anc = in ? (~0ull >> (63 - lane)) : 0ull;
-    par = lane >= 1 ? lane - 1 : 0;
-  }
+  const NodeTree t = node_tree(f.kind, f.id, W);
   int32_t* path = p.accept_path + (size_t)b * W;
-  if (!ok) {
+  if (!t.ok) {
     if (in) path[lane] = -1;
     if (lane == 0) {
       p.accept_len[b] = -1;
@@ -146,23 +273,11 @@ __device__ __forceinline__ int wave_accept(const AcceptParams& p, int b, const P
     }
     return -1;
   }
-  const bool match = in && lane >= 1 && f.draft >= 0 && f.draft == s_tgt[par];
-  const uint64_t mm = __ballot(match) | 1ull;
-  const bool acc = in && (anc & ~mm) == 0ull;
-  const int depth = __popcll(anc) - 1;
-  const int key = wave_max_int(acc ? depth * 64 + (63 - lane) : -1);
+  const bool match = in && lane >= 1 && f.draft >= 0 && f.draft == s_tgt[t.par];
+  const int key = deepest_good(__ballot(match), t, W);
   const int best = 63 - (key & 63);
   const int len = key >> 6;
-  const uint64_t ab = shfl64(anc, best);
-  // Path nodes write themselves to their depth; positions past the accepted
-  // length are padded by the lane of the same index (a different address
-  // even when that lane is itself a path node: its depth is <= len < lane).
-  if (in && ((ab >> lane) & 1ull)) {
-    const int pos = __popcll(ab & ((1ull << lane) - 1ull));
-    path[pos] = lane;
-    s_path[pos] = lane;
-  }
-  if (in && lane > len) path[lane] = -1;
+  write_path(shfl64(t.anc, best), len, W, path, s_path);
   if (lane == 0) {
     p.accept_len[b] = len;
     p.bonus_id[b] = s_tgt[best];
@@ -219,7 +334,7 @@ __device__ __forceinline__ void block_commit(const CommitParams& p, int b, const
   }
 }
 
-__global__ __launch_bounds__(256) void accept_kernel(AcceptParams p) {
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptParams p) {
   __shared__ int s_tgt[MTP_MAX_W];
   __shared__ int s_path[MTP_MAX_W];
   const int b = blockIdx.x;
@@ -257,7 +372,7 @@ constexpr int kAcceptScratchInts = 4 * MTP_MAX_W + 2;
 // tensor); the commit is then only stores.
 __device__ __forceinline__ void accept_commit_seq(const AcceptParams& ap, const CommitParams& cp, int b,
                                          int* sm) {
-  constexpr int kPre = 8;
+  constexpr int kPre = 4;
   int* s_tgt = sm;
   int* s_path = sm + MTP_MAX_W;
   int* s_pos = sm + 2 * MTP_MAX_W;  // path position of a block row, -1 if not committed
@@ -343,7 +458,7 @@ __device__ __forceinline__ void accept_commit_seq(const AcceptParams& ap, const 
   }
 }
 
-__global__ __launch_bounds__(256) void accept_commit_kernel(AcceptParams ap, CommitParams cp) {
+__global__ __launch_bounds__(kAcceptThreads) void accept_commit_kernel(AcceptParams ap, CommitParams cp) {
   __shared__ int sm[kAcceptScratchInts];
   accept_commit_seq(ap, cp, blockIdx.x, sm);
 }

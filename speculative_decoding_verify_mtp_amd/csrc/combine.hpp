@@ -3,7 +3,7 @@
 // lse = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s).  Sequences with a malformed
 // mask or context length get NaN rows.
 //
-// One wave per row.  Pass 1 spreads the splits over the lanes (one split per
+// One wave per row, `rows` rows per workgroup (waves past them idle).  Pass 1 spreads the splits over the lanes (one split per
 // lane) for M and the denominator.  Pass 2 splits the wave into four groups of
 // sixteen lanes: group q takes splits q, q+4, ..., each lane D/16 consecutive
 // accumulators, so every load is 16-byte wide and many are in flight; the
@@ -20,12 +20,14 @@ namespace mtpv {
 // kStream = true : pieces of the stream kernel, [pieces, rows_block] rows,
 //                  located through the segment table.
 template <int D, bool kStream>
-__device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamParams& sp, unsigned block) {
+__device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamParams& sp, unsigned block,
+                                             int rows) {
   constexpr int VPL = D / 16;  // accumulators per lane per split
   const int lane = threadIdx.x & 63;
   const int gq = lane >> 4, gl = lane & 15;
-  const size_t row = (size_t)block * 4 + (threadIdx.x >> 6);
-  if (row >= (size_t)p.B * p.W * p.Hq) return;
+  const int wv = threadIdx.x >> 6;
+  const size_t row = (size_t)block * rows + wv;
+  if (wv >= rows || row >= (size_t)p.B * p.W * p.Hq) return;
   const int h = (int)(row % p.Hq);
   const size_t bw = row / p.Hq;
   const int w = (int)(bw % p.W);
@@ -191,22 +193,26 @@ __device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamPa
 
 template <int D, bool kStream>
 __global__ __launch_bounds__(256) void attn_combine(AttnParams p, StreamParams sp) {
-  combine_rows<D, kStream>(p, sp, blockIdx.x);
+  combine_rows<D, kStream>(p, sp, blockIdx.x, blockDim.x >> 6);
 }
 
-// The step's second launch: combine workgroups for every output row, then
-// one acceptance + commit workgroup per sequence.  The two parts touch
-// disjoint data (the commit writes cache slots at or past each context
-// length and ctx_lens_out, which must not alias the ctx_lens the combine
-// reads), so they run side by side.
+// The step's second launch: one acceptance + commit workgroup per sequence
+// (first, so that they are dispatched first: they hold the longest chain of
+// dependent loads), then combine workgroups for every output row.  The two
+// parts touch disjoint data (the commit writes cache slots at or past each
+// context length and ctx_lens_out, which must not alias the ctx_lens the
+// combine reads), so they run side by side.  A combine workgroup takes
+// combine_rows_per_block rows, chosen so that all workgroups fit on the
+// compute units at once when the rows are few: the combine is bound by load
+// latency, and a compute unit keeps only so many loads in flight.
 template <int D, bool kStream>
-__global__ __launch_bounds__(256) void finish_kernel(AttnParams p, StreamParams sp, AcceptParams ap,
-                                                     CommitParams cp, unsigned combine_blocks) {
+__global__ __launch_bounds__(kAcceptThreads) void finish_kernel(AttnParams p, StreamParams sp, AcceptParams ap,
+                                                     CommitParams cp, int combine_rows_per_block) {
   __shared__ int sm[kAcceptScratchInts];
-  if (blockIdx.x < combine_blocks)
-    combine_rows<D, kStream>(p, sp, blockIdx.x);
+  if ((int)blockIdx.x < p.B)
+    accept_commit_seq(ap, cp, (int)blockIdx.x, sm);
   else
-    accept_commit_seq(ap, cp, (int)(blockIdx.x - combine_blocks), sm);
+    combine_rows<D, kStream>(p, sp, blockIdx.x - p.B, combine_rows_per_block);
 }
 
 }  // namespace mtpv

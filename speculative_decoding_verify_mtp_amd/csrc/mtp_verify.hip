@@ -2,6 +2,7 @@
 // kernel launches for the C ABI declared in include/mtp_verify.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -13,6 +14,7 @@
 #include "attn_valu.hpp"
 #include "combine.hpp"
 #include "common.hpp"
+#include "hybrid.hpp"
 #include "mtp_verify.h"
 
 namespace {
@@ -281,8 +283,20 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm) {
   }
 }
 
-unsigned combine_blocks(const AttnParams& p) {
-  return (unsigned)(((size_t)p.B * p.W * p.Hq + 3) / 4);
+// Workgroups of a combine launch with `rows` output rows (waves) per workgroup.
+unsigned combine_blocks(const AttnParams& p, int rows = 4) {
+  return (unsigned)(((size_t)p.B * p.W * p.Hq + rows - 1) / rows);
+}
+
+// Rows per combine workgroup of the step's finish launch.  Its workgroups
+// have kAcceptThreads threads, one per compute unit at a time; the rows are
+// spread so that the combine workgroups and the B acceptance workgroups fit
+// on the compute units together, within [4, one row per wave].
+int finish_combine_rows(const AttnParams& p) {
+  const long rows = (long)p.B * p.W * p.Hq;
+  const long free_cus = std::max(1L, (long)kCUs - p.B);
+  const long per = (rows + free_cus - 1) / free_cus;
+  return (int)std::min<long>(kAcceptThreads / kWave, std::max(4L, per));
 }
 
 void launch_combine(const Attn& a, int D, hipStream_t strm) {
@@ -390,7 +404,32 @@ mtp_status mtp_accept(const mtp_shape* shape, const float* logits, int32_t V,
   const mtp_status st = fill_accept(shape, logits, V, draft_ids, mask_kind, mask_ids, accept_len,
                                     accept_path, bonus_id, ap);
   if (st != MTP_OK || shape->B == 0) return st;
-  accept_kernel<<<dim3(shape->B), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(ap);
+  accept_kernel<<<dim3(shape->B), dim3(kAcceptThreads), 0, static_cast<hipStream_t>(stream)>>>(ap);
+  return launch_status();
+}
+
+mtp_status mtp_accept_hybrid(const mtp_shape* shape, const float* draft_logits,
+                             const float* logits, int32_t V, const int32_t* draft_ids,
+                             const uint8_t* mask_kind, const int32_t* mask_ids, float tau,
+                             int32_t min_prefix, int32_t* accept_len, int32_t* accept_path,
+                             int32_t* bonus_id, int32_t* conf_len, void* stream) {
+  if (shape == nullptr) return MTP_ERR_NULL;
+  if (shape->B > 0 && (!draft_logits || !conf_len)) return MTP_ERR_NULL;
+  if (tau != tau) return MTP_ERR_SHAPE;
+  AcceptParams ap;
+  // the greedy checks, with a stand-in for the optional verifier logits
+  const mtp_status st = fill_accept(shape, logits != nullptr ? logits : draft_logits, V, draft_ids,
+                                    mask_kind, mask_ids, accept_len, accept_path, bonus_id, ap);
+  if (st != MTP_OK || shape->B == 0) return st;
+  ap.logits = logits;
+  HybridParams hp;
+  hp.draft_logits = draft_logits;
+  hp.conf_len = conf_len;
+  hp.tau = tau;
+  hp.min_prefix = min_prefix;
+  const int ntask = (shape->W - 1) + (logits != nullptr ? shape->W : 0);
+  const int threads = kWave * std::min(16, std::max(1, ntask));
+  accept_hybrid_kernel<<<dim3(shape->B), dim3(threads), 0, static_cast<hipStream_t>(stream)>>>(ap, hp);
   return launch_status();
 }
 
@@ -423,7 +462,7 @@ mtp_status mtp_accept_commit(const mtp_shape* shape, const float* logits, int32_
   st = fill_commit(shape, k_new, v_new, accept_len, accept_path, block_table, ctx_lens_in,
                    ctx_lens_out, skip_root, k_cache, v_cache, true, cp);
   if (st != MTP_OK || shape->B == 0) return st;
-  accept_commit_kernel<<<dim3(shape->B), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(ap, cp);
+  accept_commit_kernel<<<dim3(shape->B), dim3(kAcceptThreads), 0, static_cast<hipStream_t>(stream)>>>(ap, cp);
   return launch_status();
 }
 
@@ -451,16 +490,16 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
   launch_partial(a, shape->D, shape->dtype, shape->B, strm);
   if (ctx_lens_out == ctx_lens_in) {  // the combine reads what the commit writes: serialise
     launch_combine(a, shape->D, strm);
-    accept_commit_kernel<<<dim3(shape->B), dim3(256), 0, strm>>>(ap, cp);
+    accept_commit_kernel<<<dim3(shape->B), dim3(kAcceptThreads), 0, strm>>>(ap, cp);
   } else {
-    const unsigned cb = combine_blocks(a.p);
-    const dim3 fgrid(cb + (unsigned)shape->B), block(256);
+    const int crows = finish_combine_rows(a.p);
+    const dim3 fgrid((unsigned)shape->B + combine_blocks(a.p, crows)), block(kAcceptThreads);
     if (a.pl.kernel == kMfmaStream)
-      finish_kernel<128, true><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, cb);
+      finish_kernel<128, true><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);
     else if (shape->D == 128)
-      finish_kernel<128, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, cb);
+      finish_kernel<128, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);
     else
-      finish_kernel<64, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, cb);
+      finish_kernel<64, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);
   }
   return launch_status();
 }

@@ -23,8 +23,8 @@ DEV_BAD_MASK, DEV_BAD_CTX, DEV_BAD_PAGE, DEV_BAD_ACCEPT = 1, 2, 4, 8
 
 EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_size",
            "mtp_verify_attn", "mtp_verify_attn_partial", "mtp_verify_attn_combine",
-           "mtp_accept", "mtp_kv_commit", "mtp_accept_commit", "mtp_verify_step",
-           "mtp_get_device_status")
+           "mtp_accept", "mtp_accept_hybrid", "mtp_kv_commit", "mtp_accept_commit",
+           "mtp_verify_step", "mtp_get_device_status")
 _ATTN_FN = {"both": "mtp_verify_attn", "partial": "mtp_verify_attn_partial",
             "combine": "mtp_verify_attn_combine"}
 
@@ -69,6 +69,9 @@ def load() -> ctypes.CDLL:
         getattr(lib, fn).argtypes = [sp] + [_vp] * 11 + [_vp, _sz, _vp]
     lib.mtp_accept.restype = _i32
     lib.mtp_accept.argtypes = [sp, _vp, _i32] + [_vp] * 6 + [_vp]
+    lib.mtp_accept_hybrid.restype = _i32
+    lib.mtp_accept_hybrid.argtypes = ([sp, _vp, _vp, _i32] + [_vp] * 3
+                                      + [ctypes.c_float, _i32] + [_vp] * 4 + [_vp])
     lib.mtp_kv_commit.restype = _i32
     lib.mtp_kv_commit.argtypes = [sp] + [_vp] * 7 + [_i32, _vp, _vp, _vp]
     lib.mtp_accept_commit.restype = _i32
@@ -209,6 +212,28 @@ def accept(logits, draft_ids, mask_kind, mask_ids, *, accept_len=None, accept_pa
         ctypes.byref(cs), _ptr(logits), V, _ptr(draft_ids), _ptr(mask_kind), _ptr(mask_ids),
         _ptr(accept_len), _ptr(accept_path), _ptr(bonus_id), _stream(stream)))
     return accept_len, accept_path, bonus_id
+
+
+def accept_hybrid(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau, min_prefix, *,
+                  accept_len=None, accept_path=None, bonus_id=None, conf_len=None, stream=None):
+    """Confidence-threshold / hybrid acceptance; ``logits`` may be None.  Returns
+    (accept_len [B], accept_path [B,W], bonus_id [B], conf_len [B]) int32."""
+    lib = load()
+    B, W, V = draft_logits.shape
+    dev = draft_logits.device
+    if logits is not None and tuple(logits.shape) != (B, W, V):
+        raise ValueError("logits and draft_logits must have the same shape")
+    new = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)  # noqa: E731
+    accept_len = new(B) if accept_len is None else accept_len
+    accept_path = new(B, W) if accept_path is None else accept_path
+    bonus_id = new(B) if bonus_id is None else bonus_id
+    conf_len = new(B) if conf_len is None else conf_len
+    cs = _accept_shape(draft_ids)
+    _check("mtp_accept_hybrid", lib.mtp_accept_hybrid(
+        ctypes.byref(cs), _ptr(draft_logits), _ptr(logits), V, _ptr(draft_ids), _ptr(mask_kind),
+        _ptr(mask_ids), float(tau), int(min_prefix), _ptr(accept_len), _ptr(accept_path),
+        _ptr(bonus_id), _ptr(conf_len), _stream(stream)))
+    return accept_len, accept_path, bonus_id, conf_len
 
 
 def _commit_shape(k_new, k_cache, block_table) -> Shape:

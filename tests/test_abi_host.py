@@ -92,6 +92,15 @@ def test_null_pointers_and_small_workspace(L):
     need = ws(L, s)[1]
     assert L.mtp_verify_attn(ctypes.byref(s), *([fake] * 10), None, bad, need, None) == 4
     assert L.mtp_accept(ctypes.byref(s), fake, 0, *([fake] * 6), None) == 2
+    hyb = L.mtp_accept_hybrid
+    assert hyb(None, fake, fake, 10, *([fake] * 3), 0.9, 1, *([fake] * 4), None) == 1
+    # draft_logits and conf_len are required; the verifier logits are optional
+    assert hyb(ctypes.byref(s), None, fake, 10, *([fake] * 3), 0.9, 1, *([fake] * 4), None) == 1
+    assert hyb(ctypes.byref(s), fake, None, 10, *([fake] * 3), 0.9, 1, *([fake] * 3), None,
+               None) == 1
+    assert hyb(ctypes.byref(s), fake, None, 10, *([fake] * 3), float("nan"), 1, *([fake] * 4),
+               None) == 2
+    assert hyb(ctypes.byref(s), fake, None, 0, *([fake] * 3), 0.9, 1, *([fake] * 4), None) == 2
 
 
 def test_empty_batch_needs_no_pointers(L):
@@ -99,6 +108,8 @@ def test_empty_batch_needs_no_pointers(L):
     assert L.mtp_verify_attn(ctypes.byref(s), *([None] * 11), None, 0, None) == 0
     assert L.mtp_accept(ctypes.byref(s), None, 10, *([None] * 6), None) == 0
     assert L.mtp_kv_commit(ctypes.byref(s), *([None] * 7), 0, None, None, None) == 0
+    assert L.mtp_accept_hybrid(ctypes.byref(s), None, None, 10, *([None] * 3), 0.9, 1,
+                               *([None] * 4), None) == 0
 
 
 def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):

@@ -185,6 +185,76 @@ def test_accept_argmax_ties_take_the_smallest_id():
 
 
 # ----------------------------------------------------------------------------
+# confidence-threshold / hybrid acceptance
+# ----------------------------------------------------------------------------
+
+HYBRID = [
+    W_("hyb_chain", B=16, W=8, ctx_lo=1, ctx_hi=1, conf_p=0.85),
+    W_("hyb_tree", B=16, W=32, ctx_lo=1, ctx_hi=1, masks="tree", conf_p=0.9),
+    W_("hyb_tree_w64", B=8, W=64, ctx_lo=1, ctx_hi=1, masks="tree", tree_depth=63,
+       match_p=0.9, conf_p=0.97),
+    W_("hyb_mixed_v7", B=16, W=16, ctx_lo=1, ctx_hi=1, masks="mixed", vocab=7),
+    W_("hyb_mask_tokens", B=8, W=12, ctx_lo=1, ctx_hi=1, conf_p=1.0, mask_token_rows=5),
+    W_("hyb_w1", B=4, W=1, ctx_lo=1, ctx_hi=1),
+    W_("hyb_vocab_odd", B=6, W=9, ctx_lo=1, ctx_hi=1, masks="segment", vocab=1001),
+    W_("hyb_vocab_big", B=2, W=8, ctx_lo=1, ctx_hi=1, vocab=50000),
+]
+
+
+def oracle_hybrid(inp, tau, m, with_logits=True):
+    host = inp["host"]
+    return O.accept_hybrid(f64(inp["draft_logits"]), f64(inp["logits"]) if with_logits else None,
+                           host["draft_ids"], host["mask_kind"], host["mask_ids"], tau, m)
+
+
+def assert_hybrid_equal(got, ref, tau, conf):
+    live = conf[:, 1:]
+    assert np.all(np.abs(live - tau) > 1e-4), "a confidence lies on the threshold"
+    assert_accept_equal(got[:3], ref[:3])
+    assert np.array_equal(ints(got[3]), ref[3]), f"conf_len {ints(got[3])} != {ref[3]}"
+
+
+@pytest.mark.parametrize("with_logits", [True, False])
+@pytest.mark.parametrize("tau,m", [(0.9, 1), (0.9, 3), (0.5, 2), (0.97, 1), (1.5, 1), (0.0, 4)])
+@pytest.mark.parametrize("wl", HYBRID, ids=[w.name for w in HYBRID])
+def test_hybrid_accept_bit_exact(wl, tau, m, with_logits):
+    inp = gpu_inputs(wl.scaled(D=64, Hq=2, Hkv=2), 13)
+    got = lib.accept_hybrid(inp["draft_logits"], inp["logits"] if with_logits else None,
+                            inp["draft_ids"], inp["mask_kind"], inp["mask_ids"], tau, m)
+    torch.cuda.synchronize()
+    conf = O.draft_confidence(f64(inp["draft_logits"]), inp["host"]["draft_ids"])
+    conf[inp["host"]["draft_ids"] < 0] = 2.0  # mask tokens decide nothing near tau
+    assert_hybrid_equal(got, oracle_hybrid(inp, tau, m, with_logits), tau, conf)
+
+
+def test_hybrid_confident_outputs_feed_the_commit():
+    """A confidence-branch acceptance commits through mtp_kv_commit like a
+    verified one: the h drafts' rows (root first) land in the cache."""
+    wl = W_("hyb_commit", B=6, Hq=4, Hkv=2, W=12, ctx_lo=3, ctx_hi=90, masks="mixed",
+            conf_p=0.95)
+    inp = gpu_inputs(wl, 17)
+    n, path, bonus, h = lib.accept_hybrid(inp["draft_logits"], None, inp["draft_ids"],
+                                          inp["mask_kind"], inp["mask_ids"], 0.9, 1)
+    ref = oracle_hybrid(inp, 0.9, 1, with_logits=False)
+    assert np.array_equal(ints(n), ref[0]) and np.array_equal(ints(path), ref[1])
+    keep = ints(n) >= 0
+    n = torch.where(n >= 0, n, torch.zeros_like(n))  # unconfident sequences: the root only
+    path = path.clone()
+    path[:, 0] = 0
+    kc, vc = inp["k_cache"].clone(), inp["v_cache"].clone()
+    ctx_out = lib.kv_commit(inp["k_new"], inp["v_new"], n, path, inp["block_table"],
+                            inp["ctx_lens"], kc, vc)
+    torch.cuda.synchronize()
+    host = inp["host"]
+    rk, rv, rctx = O.kv_commit(raw(inp["k_cache"]), raw(inp["v_cache"]), raw(inp["k_new"]),
+                               raw(inp["v_new"]), ints(n), ints(path), host["block_table"],
+                               host["ctx_lens"], False)
+    assert np.array_equal(ints(ctx_out), rctx)
+    assert np.array_equal(raw(kc), rk) and np.array_equal(raw(vc), rv)
+    assert keep.any() and (ints(n)[keep] >= 1).any()
+
+
+# ----------------------------------------------------------------------------
 # commit
 # ----------------------------------------------------------------------------
 
