@@ -50,6 +50,9 @@ What it computes, step by step, in the notation of the pages:
   without the verifier, otherwise the greedy verification above decides
   (BitMTP §3.3 hybrid decoding; Multi-Byte Prediction §3.1 byte acceptance).
 
+* Nested KV4 / KV8 cache (``quantize_nested``, ``verify_attention_nested``,
+  ``kv_commit_nested``): BitNest §3.4 / §A.2, see the section at the end.
+
 * Commit (``kv_commit``).  The K/V rows of the accepted path, root first, are
   copied to logical positions L, L+1, ..., L+a; rejected rows are never
   written and the KV boundary advances by a+1 (BitMTP §3.4 M2: accepted draft
@@ -177,18 +180,14 @@ def attend(q: np.ndarray, keys: np.ndarray, values: np.ndarray, mask: np.ndarray
     return out, lse, p
 
 
-def verify_attention(q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new,
-                     mask_kind, mask_ids, scale=None, seg_lookback=-1):
-    """Verify attention for a batch.
-
-    q [B,W,Hq,D]; k_cache/v_cache [pages,16,Hkv,D]; block_table [B,max_pages];
-    ctx_lens [B]; k_new/v_new [B,W,Hkv,D]; mask_kind [B]; mask_ids [B,W].
-    Returns out [B,W,Hq,D] and lse [B,W,Hq] in fp64."""
+def attention_over(q, committed, k_new, v_new, mask_kind, mask_ids, scale=None, seg_lookback=-1):
+    """Verify attention for a batch whose committed rows come from
+    ``committed(b, L) -> (keys [L,Hkv,D], values [L,Hkv,D])`` (fp64)."""
     q = np.asarray(q, dtype=np.float64)
     k_new = np.asarray(k_new, dtype=np.float64)
     v_new = np.asarray(v_new, dtype=np.float64)
     B, W, Hq, D = q.shape
-    Hkv = k_cache.shape[2]
+    Hkv = k_new.shape[2]
     g = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(D)
@@ -198,9 +197,10 @@ def verify_attention(q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new,
         kind, ids = int(mask_kind[b]), np.asarray(mask_ids[b])
         if not mask_is_valid(kind, ids):
             continue
-        L = int(ctx_lens[b])
-        keys = np.concatenate([gather_committed(k_cache, block_table[b], L), k_new[b]], axis=0)
-        vals = np.concatenate([gather_committed(v_cache, block_table[b], L), v_new[b]], axis=0)
+        ck, cv = committed(b)
+        L = ck.shape[0]
+        keys = np.concatenate([ck, k_new[b]], axis=0)
+        vals = np.concatenate([cv, v_new[b]], axis=0)
         mask = dense_mask(L, block_visibility(kind, ids, seg_lookback))
         for h in range(Hq):
             kvh = h // g
@@ -208,6 +208,20 @@ def verify_attention(q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new,
             out[b, :, h, :] = o
             lse[b, :, h] = l
     return out, lse
+
+
+def verify_attention(q, k_cache, v_cache, block_table, ctx_lens, k_new, v_new,
+                     mask_kind, mask_ids, scale=None, seg_lookback=-1):
+    """Verify attention for a batch.
+
+    q [B,W,Hq,D]; k_cache/v_cache [pages,16,Hkv,D]; block_table [B,max_pages];
+    ctx_lens [B]; k_new/v_new [B,W,Hkv,D]; mask_kind [B]; mask_ids [B,W].
+    Returns out [B,W,Hq,D] and lse [B,W,Hq] in fp64."""
+    def committed(b):
+        L = int(ctx_lens[b])
+        return (gather_committed(k_cache, block_table[b], L),
+                gather_committed(v_cache, block_table[b], L))
+    return attention_over(q, committed, k_new, v_new, mask_kind, mask_ids, scale, seg_lookback)
 
 
 # ----------------------------------------------------------------------------
@@ -260,17 +274,14 @@ def accept(logits, draft_ids, mask_kind, mask_ids):
 # commit
 # ----------------------------------------------------------------------------
 
-def kv_commit(k_cache, v_cache, k_new, v_new, accept_len, accept_path, block_table,
-              ctx_lens, skip_root=False):
-    """Copies the accepted rows' K/V bytes into the cache pages.
-
-    Works on the raw element arrays (any dtype: the copy is exact).  Returns
-    (k_cache', v_cache', ctx_lens') as new arrays; the inputs are not
-    modified."""
-    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+def commit_writes(accept_len, accept_path, block_table, ctx_lens, num_pages, skip_root=False):
+    """The commit's writes as (b, page, slot, block row) and the new context
+    lengths.  A sequence whose accepted length or path is out of range, or
+    one of whose target slots is unmapped, writes nothing and keeps its
+    length."""
     ctx = np.array(ctx_lens, dtype=np.int64, copy=True)
     B, W = accept_path.shape
-    num_pages = kc.shape[0]
+    out = []
     for b in range(B):
         a = int(accept_len[b])
         if a < 0 or a > W - 1:
@@ -288,13 +299,27 @@ def kv_commit(k_cache, v_cache, k_new, v_new, accept_len, accept_path, block_tab
             if not (0 <= page < num_pages):
                 writes = None
                 break
-            writes.append((page, slot, row))
+            writes.append((b, page, slot, row))
         if writes is None:
             continue
-        for page, slot, row in writes:
-            kc[page, slot] = k_new[b, row]
-            vc[page, slot] = v_new[b, row]
+        out.extend(writes)
         ctx[b] = L + a + 1
+    return out, ctx
+
+
+def kv_commit(k_cache, v_cache, k_new, v_new, accept_len, accept_path, block_table,
+              ctx_lens, skip_root=False):
+    """Copies the accepted rows' K/V bytes into the cache pages.
+
+    Works on the raw element arrays (any dtype: the copy is exact).  Returns
+    (k_cache', v_cache', ctx_lens') as new arrays; the inputs are not
+    modified."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    writes, ctx = commit_writes(accept_len, accept_path, block_table, ctx_lens, kc.shape[0],
+                                skip_root)
+    for b, page, slot, row in writes:
+        kc[page, slot] = k_new[b, row]
+        vc[page, slot] = v_new[b, row]
     return kc, vc, ctx
 
 
@@ -377,3 +402,123 @@ def accept_hybrid(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau, min
         elif logits is not None:
             acc_len[b], path[b], bonus[b] = v_len[b], v_path[b], v_bonus[b]
     return acc_len, path, bonus, conf_len
+
+
+# ----------------------------------------------------------------------------
+# nested KV4 / KV8 cache
+# ----------------------------------------------------------------------------
+#
+# "BitNest: Bit-Nested Speculative Decoding for Memory-Efficient LLM Inference
+# Acceleration", §3.4 and §A.2.  Every cached K or V vector of one token and
+# one KV head is quantized once, when it is written: symmetric round-to-nearest
+# at a per-vector scale s gives the 4-bit base codes (the KV4 view, s * q4);
+# the base's residual is quantized again at the sixteen-times finer scale s/16
+# into 4-bit refinement codes, and base + refinement is the KV8 view,
+# (s/16) * (16 q4 + qr).  The two code planes are stored separately, so a
+# reader takes the base alone (KV4) or both (KV8).
+#
+# The pages leave the scale rule and the rounding open; the reading used here:
+#   s = max|x| / 7 (so the base uses codes -7..7), t = x / s, q4 = rint(t),
+#   qr = clamp(rint(16 t) - 16 q4, -8, 7), rint = round half to even, all in
+#   fp32 (the codes are integers decided by floating point: both sides decide
+#   in fp32).  A zero vector has s = 0 and zero codes.
+# Storage: codes + 8 as unsigned nibbles, two per byte, the even element in
+# the low nibble; planes [pages, Hkv, 16, D/2] bytes; scales [pages, Hkv, 16]
+# fp32 (the 16 slots of one page and head are contiguous).
+# Reading policy (§3.4, §A.2): verification reads KV8; drafting reads KV4;
+# "Recent-N" reads the N most recent committed tokens in KV8 and older ones
+# in KV4.  kv8_recent = -1 means all KV8, 0 all KV4, N > 0 Recent-N.
+
+NEST_OFFSET = 8
+
+
+def quantize_nested(x):
+    """x [..., D] (finite) -> base codes q4, refinement codes qr (int64, in
+    [-8, 7]) and the fp32 scale s [...]."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    s = (amax / np.float32(7.0)).astype(np.float32)
+    live = s > 0
+    t = (x / np.where(live, s, np.float32(1.0))[..., None]).astype(np.float32)
+    q4 = np.rint(t)
+    qr = np.clip(np.rint(t * np.float32(16.0)) - 16.0 * q4, -8, 7)
+    q4 = np.where(live[..., None], q4, 0).astype(np.int64)
+    qr = np.where(live[..., None], qr, 0).astype(np.int64)
+    return q4, qr, s
+
+
+def pack_nibbles(codes):
+    """[..., D] codes in [-8, 7] -> [..., D/2] bytes (code + 8, even element low)."""
+    u = (np.asarray(codes) + NEST_OFFSET).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed):
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = (packed & 15).astype(np.int64) - NEST_OFFSET
+    out[..., 1::2] = (packed >> 4).astype(np.int64) - NEST_OFFSET
+    return out
+
+
+def nested_planes(cache):
+    """Quantizes a whole [pages, 16, Hkv, D] cache into its nested planes."""
+    q4, qr, s = quantize_nested(cache)
+    return {"base": np.ascontiguousarray(pack_nibbles(q4).transpose(0, 2, 1, 3)),
+            "ref": np.ascontiguousarray(pack_nibbles(qr).transpose(0, 2, 1, 3)),
+            "scale": np.ascontiguousarray(s.transpose(0, 2, 1))}
+
+
+def dequantize_nested(planes, level):
+    """KV8 (level 8) or KV4 (level 4) view of nested planes as a
+    [pages, 16, Hkv, D] fp64 cache (exact)."""
+    q4 = unpack_nibbles(planes["base"]).astype(np.float64)
+    s = np.asarray(planes["scale"], dtype=np.float64)[..., None]
+    if level == 4:
+        v = s * q4
+    elif level == 8:
+        qr = unpack_nibbles(planes["ref"]).astype(np.float64)
+        v = s * (16.0 * q4 + qr) / 16.0
+    else:
+        raise ValueError("level must be 4 or 8")
+    return v.transpose(0, 2, 1, 3)
+
+
+def verify_attention_nested(q, k_planes, v_planes, block_table, ctx_lens, k_new, v_new,
+                            mask_kind, mask_ids, scale=None, seg_lookback=-1, kv8_recent=-1):
+    """Verify attention over a nested cache: committed token t of a sequence
+    with context L is read in KV8 when kv8_recent < 0 or t >= L - kv8_recent,
+    else in KV4; the block's own rows (k_new, v_new) are used as given."""
+    views = {lvl: (dequantize_nested(k_planes, lvl), dequantize_nested(v_planes, lvl))
+             for lvl in (4, 8)}
+
+    def committed(b):
+        L = int(ctx_lens[b])
+        k8 = gather_committed(views[8][0], block_table[b], L)
+        v8 = gather_committed(views[8][1], block_table[b], L)
+        if kv8_recent < 0:
+            return k8, v8
+        k4 = gather_committed(views[4][0], block_table[b], L)
+        v4 = gather_committed(views[4][1], block_table[b], L)
+        old = np.arange(L) < L - kv8_recent
+        return np.where(old[:, None, None], k4, k8), np.where(old[:, None, None], v4, v8)
+
+    return attention_over(q, committed, k_new, v_new, mask_kind, mask_ids, scale, seg_lookback)
+
+
+def kv_commit_nested(k_planes, v_planes, k_new, v_new, accept_len, accept_path, block_table,
+                     ctx_lens, skip_root=False):
+    """The commit of ``kv_commit`` into a nested cache: each accepted row is
+    quantized (``quantize_nested``) into its slot's codes and scale.  Returns
+    new plane dicts and the new context lengths."""
+    kp = {k: np.array(v, copy=True) for k, v in k_planes.items()}
+    vp = {k: np.array(v, copy=True) for k, v in v_planes.items()}
+    writes, ctx = commit_writes(accept_len, accept_path, block_table, ctx_lens,
+                                kp["scale"].shape[0], skip_root)
+    for b, page, slot, row in writes:
+        for planes, src in ((kp, k_new), (vp, v_new)):
+            q4, qr, sc = quantize_nested(np.asarray(src[b, row], dtype=np.float32))
+            planes["base"][page, :, slot] = pack_nibbles(q4)
+            planes["ref"][page, :, slot] = pack_nibbles(qr)
+            planes["scale"][page, :, slot] = sc
+    return kp, vp, ctx

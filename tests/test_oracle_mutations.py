@@ -12,6 +12,7 @@ import pytest
 
 from oracle import verify_oracle as O
 from tests import test_oracle_hybrid as H
+from tests import test_oracle_nested as N
 from tests import test_oracle_pins as P
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -114,6 +115,50 @@ def _hybrid_strict_min_prefix(draft_logits, logits, draft_ids, mask_kind, mask_i
     return _orig(draft_logits, logits, draft_ids, mask_kind, mask_ids, tau, min_prefix + 1)
 
 
+def _quantize_scale_over_8(x):
+    x = np.asarray(x, dtype=np.float32)
+    s = (np.abs(x).max(axis=-1) / np.float32(8.0)).astype(np.float32)
+    live = s > 0
+    t = (x / np.where(live, s, np.float32(1.0))[..., None]).astype(np.float32)
+    q4 = np.clip(np.rint(t), -8, 7)
+    qr = np.clip(np.rint(t * np.float32(16.0)) - 16.0 * q4, -8, 7)
+    return (np.where(live[..., None], q4, 0).astype(np.int64),
+            np.where(live[..., None], qr, 0).astype(np.int64), s)
+
+
+def _quantize_half_away(x):
+    x = np.asarray(x, dtype=np.float32)
+    s = (np.abs(x).max(axis=-1) / np.float32(7.0)).astype(np.float32)
+    live = s > 0
+    t = (x / np.where(live, s, np.float32(1.0))[..., None]).astype(np.float32)
+    q4 = np.sign(t) * np.floor(np.abs(t) + 0.5)
+    qr = np.clip(np.sign(t) * np.floor(np.abs(16 * t) + 0.5) - 16.0 * q4, -8, 7)
+    return (np.where(live[..., None], q4, 0).astype(np.int64),
+            np.where(live[..., None], qr, 0).astype(np.int64), s)
+
+
+def _pack_high_first(codes):
+    u = (np.asarray(codes) + O.NEST_OFFSET).astype(np.uint8)
+    return (u[..., 1::2] | (u[..., 0::2] << 4)).astype(np.uint8)
+
+
+def _kv8_without_refinement(planes, level, _orig=O.dequantize_nested):
+    return _orig(planes, 4)
+
+
+def _refinement_grid_eighth(planes, level, _orig=O.dequantize_nested):
+    if level != 8:
+        return _orig(planes, level)
+    q4 = O.unpack_nibbles(planes["base"]).astype(np.float64)
+    qr = O.unpack_nibbles(planes["ref"]).astype(np.float64)
+    s = np.asarray(planes["scale"], dtype=np.float64)[..., None]
+    return (s * (8.0 * q4 + qr) / 8.0).transpose(0, 2, 1, 3)
+
+
+def _recent_window_off_by_one(*args, kv8_recent=-1, _orig=O.verify_attention_nested, **kw):
+    return _orig(*args, kv8_recent=kv8_recent + 1 if kv8_recent >= 0 else kv8_recent, **kw)
+
+
 MUTANTS = [
     ("block_visibility", _tree_vis_without_self, [(P.test_tree_visibility_is_ancestor_closure, 3),
                                                   (P.test_tree_golden_fixture,)]),
@@ -134,6 +179,15 @@ MUTANTS = [
     ("accept_hybrid", _hybrid_commits_h_drafts, [(H.test_hybrid_golden_chain,),
                                                  (H.test_chain_confidence_prefix_closed_form, 0)]),
     ("accept_hybrid", _hybrid_strict_min_prefix, [(H.test_hybrid_golden_chain,)]),
+    ("quantize_nested", _quantize_scale_over_8, [(N.test_golden_rows,),
+                                                 (N.test_round_to_nearest_error_bounds, 0)]),
+    ("quantize_nested", _quantize_half_away, [(N.test_golden_rows,)]),
+    ("pack_nibbles", _pack_high_first, [(N.test_golden_rows,)]),
+    ("dequantize_nested", _kv8_without_refinement,
+     [(N.test_golden_rows,), (N.test_grid_exact_cache_reduces_to_dense_attention, "chain")]),
+    ("dequantize_nested", _refinement_grid_eighth, [(N.test_golden_rows,)]),
+    ("verify_attention_nested", _recent_window_off_by_one,
+     [(N.test_recent_window_reads_kv8_only_for_the_newest_tokens,)]),
 ]
 
 
