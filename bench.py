@@ -179,6 +179,103 @@ def bench_accept_hybrid(wl: I.Workload, inp: dict, args) -> int:
     return 0
 
 
+def nested_kv_bytes(wl: I.Workload, ctx: np.ndarray, kv8_recent: int) -> int:
+    """Committed K + V bytes a nested-cache read must move: per token and KV
+    head, D/2 base bytes and a 4-byte scale per tensor, plus D/2 refinement
+    bytes for tokens read in KV8."""
+    ctx = ctx.astype(np.int64)
+    n8 = ctx if kv8_recent < 0 else np.minimum(ctx, kv8_recent)
+    per_tensor = int(np.sum(ctx)) * (wl.D // 2 + 4) + int(np.sum(n8)) * (wl.D // 2)
+    return per_tensor * wl.Hkv * 2
+
+
+def bench_nested_attn(wl: I.Workload, inp: dict, args) -> int:
+    """Verify attention over the nested cache: the bf16 pool (replicated for a
+    cold cache, as for the step) is quantized once, untimed; then graphs of
+    R partial-kernel launches and of R whole attentions are replayed."""
+    host = inp["host"]
+    ctx = host["ctx_lens"]
+    if wl.D != 128 or wl.dtype != "bf16":
+        print("bench.py: the nested cache is built for bf16 heads of 128", file=sys.stderr)
+        return 2
+    nb = algorithmic_bytes(wl, ctx)
+    kvb = nested_kv_bytes(wl, ctx, args.kv8_recent)
+    part_bytes = nb["partial"] - nb["kv"] + kvb
+    pool = inp["k_cache"].shape[0]
+    R = 1 if args.warm else (args.replicas or max(1, math.ceil(1.0e9 / max(kvb, 1))))
+    R = min(R, max(1, (2**31 - 1) // pool))
+    kv = lib.NestedKV(pool * R, wl.Hkv, wl.D)
+    for r in range(R):
+        slots = torch.arange(pool * 16, dtype=torch.int32, device="cuda") + r * pool * 16
+        lib.kv_quantize(inp["k_cache"].reshape(pool * 16, wl.Hkv, wl.D),
+                        inp["v_cache"].reshape(pool * 16, wl.Hkv, wl.D), slots, kv)
+    bt = inp["block_table"]
+    tables = [torch.where(bt >= 0, bt + r * pool, bt).contiguous() for r in range(R)]
+    del inp["k_cache"], inp["v_cache"]
+    mc = int(ctx.max())
+    B, W, Hq, D = inp["q"].shape
+    shape = lib.VerifyShape(B, W, Hq, wl.Hkv, D, pool * R, bt.shape[1], mc, lib.MTP_BF16,
+                            inp["scale"], wl.seg_lookback, args.split_tokens)
+    ws = torch.empty(max(lib.nested_workspace_bytes(shape), 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, W, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, W, Hq), dtype=torch.float32, device="cuda")
+
+    def run(r, phase):
+        lib.verify_attn_nested(inp["q"], kv, tables[r], inp["ctx_lens"], inp["k_new"],
+                               inp["v_new"], inp["mask_kind"], inp["mask_ids"],
+                               kv8_recent=args.kv8_recent, out=out, lse=lse, workspace=ws,
+                               shape=shape, phase=phase)
+
+    res = {}
+    for phase in ("both", "partial"):
+        for r in range(R):
+            run(r, phase)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for r in range(R):
+                    run(r, phase)
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(args.steps / R))
+        for _ in range(max(1, math.ceil(args.warmup / R))):
+            g.replay()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        z.record()
+        torch.cuda.synchronize()
+        res[phase] = a.elapsed_time(z) / (reps * R)
+    if lib.device_status(clear=True) != 0:
+        print("bench.py: the device reported a data error", file=sys.stderr)
+        return 3
+    ms, pms = res["both"], res["partial"]
+    achieved = part_bytes / (pms * 1e-3) / 1e9
+    mode = {-1: "KV8"}.get(args.kv8_recent, "KV4" if args.kv8_recent == 0
+                           else f"Recent-{args.kv8_recent}")
+    rec = {
+        "metric": "nested-KV verify attention: committed KV GB/s at 1 GPU; % of HBM roofline",
+        "value": round(kvb / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": reps * R, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/Q quantized to nested KV4/KV8 planes)",
+        "config": {"workload": wl.name, "B": wl.B, "W": wl.W, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "D": wl.D, "ctx": [int(ctx.min()), int(ctx.max())], "read": mode,
+                   "kv_replicas": R, "cache": "warm" if R == 1 else "cold"},
+        "kv_bytes_per_step": kvb,
+        "bf16_kv_bytes_same_tokens": nb["kv"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_partial_nested", "kernel_us": round(pms * 1e3, 3),
+                     "algorithmic_bytes": part_bytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,9 +291,12 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only time a plain device copy of MB megabytes (HBM reference and "
                          "the FETCH_SIZE/WRITE_SIZE calibration kernel), then exit")
-    ap.add_argument("--kernel", default="step", choices=["step", "accept_hybrid"],
+    ap.add_argument("--kernel", default="step", choices=["step", "accept_hybrid", "nested_attn"],
                     help="step: the whole verify step (default); accept_hybrid: only the "
-                         "confidence/hybrid acceptance kernel, timed on its own")
+                         "confidence/hybrid acceptance kernel; nested_attn: verify attention "
+                         "over the nested KV4/KV8 cache")
+    ap.add_argument("--kv8-recent", type=int, default=-1,
+                    help="nested_attn: -1 all KV8, 0 all KV4, N the N newest tokens in KV8")
     ap.add_argument("--tau", type=float, default=0.9)
     ap.add_argument("--min-prefix", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -242,6 +342,8 @@ def main() -> int:
     inp = I.make_inputs(wl, seed, device=dev)
     if args.kernel == "accept_hybrid":
         return bench_accept_hybrid(wl, inp, args)
+    if args.kernel == "nested_attn":
+        return bench_nested_attn(wl, inp, args)
     host = inp["host"]
     ctx = host["ctx_lens"]
     nbytes = algorithmic_bytes(wl, ctx)

@@ -255,6 +255,82 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
                            int32_t* ctx_lens_out, int32_t skip_root, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* ---- Nested KV4 / KV8 cache ("BitNest: Bit-Nested Speculative Decoding for
+ * Memory-Efficient LLM Inference Acceleration", Sec. 3.4 and Sec. A.2) ----
+ *
+ * Each committed K or V vector x (one token, one KV head, D elements) is
+ * quantized once, when written: s = max|x| / 7, t = x / s,
+ * q4 = rint(t), qr = clamp(rint(16 t) - 16 q4, -8, 7) (fp32, rint = round half
+ * to even; s = 0 and zero codes for a zero vector).  KV4 = s * q4 (the base
+ * plane alone), KV8 = (s / 16) * (16 q4 + qr) (base + refinement).  Layout
+ * (all device memory, owned by the caller, 16-byte aligned):
+ *   *_base, *_ref  [num_pages, Hkv, 16, D/2] bytes: code + 8 in nibbles, two
+ *                  per byte, even element in the low nibble;
+ *   *_scale        [num_pages, Hkv, 16] fp32.
+ * Slots never written hold arbitrary bytes; no call reads them as data. */
+typedef struct mtp_nested_kv {
+  uint8_t* k_base;
+  uint8_t* k_ref;
+  float* k_scale;
+  uint8_t* v_base;
+  uint8_t* v_ref;
+  float* v_scale;
+} mtp_nested_kv;
+
+/* Quantizes n_rows K and V rows ([n_rows, Hkv, D] in shape->dtype, fp32 or
+ * bf16, finite) into the nested planes at slots[r] = page * 16 + slot (the
+ * prefill path).  Uses Hkv, D, dtype and num_pages of `shape`.  A slot
+ * outside [0, 16 * num_pages) is skipped (MTP_DEV_BAD_PAGE).  Rows sharing a
+ * slot race. */
+mtp_status mtp_kv_quantize(const mtp_shape* shape, const void* k_rows, const void* v_rows,
+                           int32_t n_rows, const int32_t* slots, const mtp_nested_kv* kv,
+                           void* stream);
+
+/* mtp_kv_commit into a nested cache: each accepted row of k_new / v_new is
+ * quantized into its slot (same validation and context update as
+ * mtp_kv_commit; `kv` is a host pointer to device plane pointers). */
+mtp_status mtp_kv_commit_nested(const mtp_shape* shape, const void* k_new, const void* v_new,
+                                const int32_t* accept_len, const int32_t* accept_path,
+                                const int32_t* block_table, const int32_t* ctx_lens_in,
+                                int32_t* ctx_lens_out, int32_t skip_root,
+                                const mtp_nested_kv* kv, void* stream);
+
+/* Workspace of mtp_verify_attn_nested (its split plan differs from the
+ * bf16-cache one). */
+mtp_status mtp_verify_attn_nested_workspace_size(const mtp_shape* shape, size_t* bytes);
+
+/* Verify attention over a nested cache (bf16 queries and block rows,
+ * D = 128).  Arguments as for mtp_verify_attn, with the committed cache given
+ * as planes.  Committed token t of a sequence with context length L is read
+ * in KV8 when kv8_recent < 0 (verification: the full cache) or
+ * t >= L - kv8_recent ("Recent-N"), else in KV4; kv8_recent = 0 reads the
+ * base plane only (drafting), and then k_ref / v_ref may be NULL.  The
+ * block's own rows (k_new, v_new) are used unquantized.  Results match
+ * attention over the dequantized cache within the bf16 tolerance. */
+mtp_status mtp_verify_attn_nested(const mtp_shape* shape, const void* q, const mtp_nested_kv* kv,
+                                  const int32_t* block_table, const int32_t* ctx_lens,
+                                  const void* k_new, const void* v_new, const uint8_t* mask_kind,
+                                  const int32_t* mask_ids, int32_t kv8_recent, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* The two launches of mtp_verify_attn_nested on their own (the partial
+ * kernel over the planes, then the combine); same arguments and checks. */
+mtp_status mtp_verify_attn_nested_partial(const mtp_shape* shape, const void* q,
+                                          const mtp_nested_kv* kv, const int32_t* block_table,
+                                          const int32_t* ctx_lens, const void* k_new,
+                                          const void* v_new, const uint8_t* mask_kind,
+                                          const int32_t* mask_ids, int32_t kv8_recent,
+                                          float* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+mtp_status mtp_verify_attn_nested_combine(const mtp_shape* shape, const void* q,
+                                          const mtp_nested_kv* kv, const int32_t* block_table,
+                                          const int32_t* ctx_lens, const void* k_new,
+                                          const void* v_new, const uint8_t* mask_kind,
+                                          const int32_t* mask_ids, int32_t kv8_recent,
+                                          float* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 /* Reads (and with clear != 0 resets) the current device's sticky status word
  * into *bits.  Synchronous: waits for all work on the device. */
 mtp_status mtp_get_device_status(uint32_t* bits, int32_t clear);

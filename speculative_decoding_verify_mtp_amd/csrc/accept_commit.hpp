@@ -285,12 +285,15 @@ __device__ __forceinline__ int wave_accept(const AcceptParams& p, int b, const P
   return len;
 }
 
-// Commit of sequence b.  Wave 0 validates (one path position per lane) and
-// publishes the copy list in LDS; then all threads copy.  When fused, `a` and
-// s_path come from the acceptance; otherwise they are read from memory.
+// Commit plan of sequence b: wave 0 validates one path position per lane
+// (row index, page mapping) and publishes the source rows (s_src), the
+// destination slots page * 16 + slot (s_dst) and the range (s_meta: last
+// position or -1, first position) in LDS; it writes the new context length.
+// Ends with a workgroup barrier.  When fused, `a_fused` and s_path come from
+// the acceptance; otherwise they are read from memory.
 template <bool kFused>
-__device__ __forceinline__ void block_commit(const CommitParams& p, int b, const Prefetch& f, int a_fused,
-                                    const int* s_path, int* s_src, int* s_dst, int* s_meta) {
+__device__ __forceinline__ void commit_plan(const CommitParams& p, int b, const Prefetch& f, int a_fused,
+                                   const int* s_path, int* s_src, int* s_dst, int* s_meta) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < kWave) {
     const int a = kFused ? a_fused : p.accept_len[b];
@@ -315,6 +318,13 @@ __device__ __forceinline__ void block_commit(const CommitParams& p, int b, const
     }
   }
   __syncthreads();
+}
+
+// Commit of sequence b: the plan, then all threads copy the accepted rows.
+template <bool kFused>
+__device__ __forceinline__ void block_commit(const CommitParams& p, int b, const Prefetch& f, int a_fused,
+                                    const int* s_path, int* s_src, int* s_dst, int* s_meta) {
+  commit_plan<kFused>(p, b, f, a_fused, s_path, s_src, s_dst, s_meta);
   const int a = s_meta[0];
   const int first = s_meta[1];
   if (a < first) return;
@@ -345,21 +355,26 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptParams p) 
   if (threadIdx.x < kWave) wave_accept(p, b, f, s_tgt, s_path);
 }
 
-__global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
-  __shared__ int s_src[MTP_MAX_W];
-  __shared__ int s_dst[MTP_MAX_W];
-  __shared__ int s_meta[2];
-  const int b = blockIdx.x;
+// Commit inputs of wave 0 (only wave 0 reads ctx_in: ctx_out may alias it).
+__device__ __forceinline__ Prefetch commit_prefetch(const CommitParams& p, int b) {
   const int lane = threadIdx.x & 63;
   Prefetch f{};
   f.page = -1;
-  if (threadIdx.x < kWave) {  // only wave 0 reads ctx_in (ctx_out may alias it)
+  if (threadIdx.x < kWave) {
     f.L = p.ctx_in[b];
     const int pi = (f.L + lane) >> 4;
     if (lane < p.W && f.L >= 0 && pi < p.max_pages)
       f.page = p.block_table[(size_t)b * p.max_pages + pi];
   }
-  block_commit<false>(p, b, f, 0, nullptr, s_src, s_dst, s_meta);
+  return f;
+}
+
+__global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
+  __shared__ int s_src[MTP_MAX_W];
+  __shared__ int s_dst[MTP_MAX_W];
+  __shared__ int s_meta[2];
+  const int b = blockIdx.x;
+  block_commit<false>(p, b, commit_prefetch(p, b), 0, nullptr, s_src, s_dst, s_meta);
 }
 
 // LDS scratch of one fused acceptance + commit, in ints.

@@ -15,6 +15,8 @@
 #include "combine.hpp"
 #include "common.hpp"
 #include "hybrid.hpp"
+#include "nested.hpp"
+#include "attn_nested_lds.hpp"
 #include "mtp_verify.h"
 
 namespace {
@@ -31,7 +33,7 @@ constexpr long kTargetWaves = 2048;
 constexpr int kMinSplit = 64;
 constexpr int kMaxSplit = 2048;
 
-enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3 };
+enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3, kMfmaNested = 4 };
 
 // Stream kernel: persistent grid sized for gfx950's 256 CUs (two workgroups
 // per CU at one row tile per wave, one at two), each workgroup streaming at
@@ -80,14 +82,23 @@ int pow2_ceil(long x) {
   return p;
 }
 
-Plan make_plan(const mtp_shape& s) {
+// `nested`: the plan of the nested-cache kernel (bf16, D = 128, LDS ring):
+// workgroups shaped as for the bf16 LDS kernel (fewer rows than a tile are
+// padded to one).
+Plan make_plan(const mtp_shape& s, bool nested = false) {
   Plan pl;
   pl.g = s.Hq / s.Hkv;
   pl.R = s.W * pl.g;
-  pl.mfma = s.dtype == MTP_BF16 && pl.R >= 16;
+  pl.mfma = nested || (s.dtype == MTP_BF16 && pl.R >= 16);
   pl.NR = 1;
   const int tiles = (pl.R + 15) / 16;
-  if (pl.mfma && s.D == 128) {
+  if (nested) {
+    pl.kernel = kMfmaNested;
+    pl.NR = tiles >= 3 ? 4 : tiles;
+    const int per = (tiles + pl.NR - 1) / pl.NR;
+    pl.RB = per >= 2 ? 2 : 1;
+    pl.nRB = (tiles + pl.NR * pl.RB - 1) / (pl.NR * pl.RB);
+  } else if (pl.mfma && s.D == 128) {
     // One workgroup of NR waves shares each K/V stage; wave w owns RB row
     // tiles.  Up to 4 waves x 2 tiles = 128 rows per row block.
     pl.kernel = kMfmaLds;
@@ -109,9 +120,9 @@ Plan make_plan(const mtp_shape& s) {
   if (s.split_tokens > 0) {
     pl.S = s.split_tokens;
   } else {
-    const long target = pl.kernel == kMfmaLds ? kTargetWorkgroups : kTargetWaves;
-    const int rows_item = pl.kernel == kMfmaLds ? 16 * pl.NR * pl.RB
-                          : pl.kernel == kMfmaDirect ? 16 * pl.RB : kValuRows;
+    const bool wg = pl.kernel == kMfmaLds || pl.kernel == kMfmaNested;
+    const long target = wg ? kTargetWorkgroups : kTargetWaves;
+    const int rows_item = wg ? 16 * pl.NR * pl.RB : pl.kernel == kMfmaDirect ? 16 * pl.RB : kValuRows;
     const long work = (long)s.B * s.Hkv * pl.nRB * (long)(s.max_ctx_len > 0 ? s.max_ctx_len : 1);
     int S = pow2_ceil((work + target - 1) / target);
     const int floor_rows = pow2_ceil(2L * rows_item);
@@ -177,6 +188,15 @@ mtp_status mtp_verify_attn_workspace_size(const mtp_shape* shape, size_t* bytes)
   return MTP_OK;
 }
 
+mtp_status mtp_verify_attn_nested_workspace_size(const mtp_shape* shape, size_t* bytes) {
+  const mtp_status st = check_shape(shape);
+  if (st != MTP_OK) return st;
+  if (bytes == nullptr) return MTP_ERR_NULL;
+  const Plan pl = make_plan(*shape, true);
+  *bytes = pl.seg_offset + pl.seg_bytes;
+  return MTP_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -193,15 +213,16 @@ mtp_status build_attn(const mtp_shape* shape, const void* q, const void* k_cache
                       const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
                       const void* k_new, const void* v_new, const uint8_t* mask_kind,
                       const int32_t* mask_ids, float* out, float* lse, void* workspace,
-                      size_t workspace_bytes, Attn& a) {
+                      size_t workspace_bytes, Attn& a, bool nested = false) {
   const mtp_status st = check_shape(shape);
   if (st != MTP_OK) return st;
   const mtp_shape& s = *shape;
+  if (nested && (s.D != 128 || s.dtype != MTP_BF16)) return MTP_ERR_UNSUPPORTED;
   if (s.B == 0) return MTP_OK;
-  if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !k_new || !v_new || !mask_kind ||
-      !mask_ids || !out || !workspace)
+  if (!q || (!nested && (!k_cache || !v_cache)) || !block_table || !ctx_lens || !k_new || !v_new ||
+      !mask_kind || !mask_ids || !out || !workspace)
     return MTP_ERR_NULL;
-  a.pl = make_plan(s);
+  a.pl = make_plan(s, nested);
   const Plan& pl = a.pl;
   if (workspace_bytes < pl.seg_offset + pl.seg_bytes || ((uintptr_t)workspace & 15) != 0)
     return MTP_ERR_WORKSPACE;
@@ -241,13 +262,21 @@ mtp_status build_attn(const mtp_shape* shape, const void* q, const void* k_cache
   return MTP_OK;
 }
 
-void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm) {
+void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
+                    const NestedAttn* na = nullptr) {
   const Plan& pl = a.pl;
   const AttnParams& p = a.p;
   const StreamParams& sp = a.sp;
   const dim3 block(256);
   const long items = (long)pl.max_splits * p.Hkv * pl.nRB;
-  if (pl.kernel == kMfmaStream) {
+  if (pl.kernel == kMfmaNested) {
+    const dim3 wgrid((unsigned)items, (unsigned)B);
+    const dim3 wblock(64 * pl.NR);
+    if (pl.RB == 2) attn_partial_nested_lds<2, 4><<<wgrid, wblock, 0, strm>>>(p, *na);
+    else if (pl.NR == 4) attn_partial_nested_lds<1, 4><<<wgrid, wblock, 0, strm>>>(p, *na);
+    else if (pl.NR == 2) attn_partial_nested_lds<1, 2><<<wgrid, wblock, 0, strm>>>(p, *na);
+    else attn_partial_nested_lds<1, 1><<<wgrid, wblock, 0, strm>>>(p, *na);
+  } else if (pl.kernel == kMfmaStream) {
     const dim3 sgrid((unsigned)pl.G);
     const dim3 sblock(64 * pl.NR);
     if (pl.RB == 2) attn_partial_stream<2, 4><<<sgrid, sblock, 0, strm>>>(p, sp);
@@ -501,6 +530,112 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
     else
       finish_kernel<64, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);
   }
+  return launch_status();
+}
+
+static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+// Checks the planes a nested-cache call needs (refinement planes unless
+// `base_only`): present and 16-byte aligned.
+static mtp_status check_nested(const mtp_nested_kv* kv, bool base_only) {
+  if (kv == nullptr || !kv->k_base || !kv->k_scale || !kv->v_base || !kv->v_scale) return MTP_ERR_NULL;
+  if (!base_only && (!kv->k_ref || !kv->v_ref)) return MTP_ERR_NULL;
+  if (!aligned16(kv->k_base) || !aligned16(kv->k_scale) || !aligned16(kv->v_base) ||
+      !aligned16(kv->v_scale) || (!base_only && (!aligned16(kv->k_ref) || !aligned16(kv->v_ref))))
+    return MTP_ERR_SHAPE;
+  return MTP_OK;
+}
+
+static mtp_status verify_attn_nested_phases(int phases, const mtp_shape* shape, const void* q,
+                                            const mtp_nested_kv* kv, const int32_t* block_table,
+                                            const int32_t* ctx_lens, const void* k_new,
+                                            const void* v_new, const uint8_t* mask_kind,
+                                            const int32_t* mask_ids, int32_t kv8_recent,
+                                            float* out, float* lse, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  Attn a;
+  mtp_status st = build_attn(shape, q, nullptr, nullptr, block_table, ctx_lens, k_new, v_new,
+                             mask_kind, mask_ids, out, lse, workspace, workspace_bytes, a, true);
+  if (st != MTP_OK || shape->B == 0) return st;
+  if (kv8_recent < -1) return MTP_ERR_SHAPE;
+  st = check_nested(kv, kv8_recent == 0);
+  if (st != MTP_OK) return st;
+  NestedAttn na;
+  na.kv = *kv;
+  na.kv8_recent = kv8_recent;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (phases & kPartial) launch_partial(a, shape->D, shape->dtype, shape->B, strm, &na);
+  if (phases & kCombine) launch_combine(a, shape->D, strm);
+  return launch_status();
+}
+
+#define MTPV_NESTED_ARGS                                                                     \
+  const mtp_shape *shape, const void *q, const mtp_nested_kv *kv, const int32_t *block_table, \
+      const int32_t *ctx_lens, const void *k_new, const void *v_new,                          \
+      const uint8_t *mask_kind, const int32_t *mask_ids, int32_t kv8_recent, float *out,      \
+      float *lse, void *workspace, size_t workspace_bytes, void *stream
+#define MTPV_NESTED_PASS                                                                      \
+  shape, q, kv, block_table, ctx_lens, k_new, v_new, mask_kind, mask_ids, kv8_recent, out, lse, \
+      workspace, workspace_bytes, stream
+
+mtp_status mtp_verify_attn_nested(MTPV_NESTED_ARGS) {
+  return verify_attn_nested_phases(kBoth, MTPV_NESTED_PASS);
+}
+
+mtp_status mtp_verify_attn_nested_partial(MTPV_NESTED_ARGS) {
+  return verify_attn_nested_phases(kPartial, MTPV_NESTED_PASS);
+}
+
+mtp_status mtp_verify_attn_nested_combine(MTPV_NESTED_ARGS) {
+  return verify_attn_nested_phases(kCombine, MTPV_NESTED_PASS);
+}
+
+mtp_status mtp_kv_quantize(const mtp_shape* shape, const void* k_rows, const void* v_rows,
+                           int32_t n_rows, const int32_t* slots, const mtp_nested_kv* kv,
+                           void* stream) {
+  const mtp_status st = check_shape(shape);
+  if (st != MTP_OK) return st;
+  if (n_rows < 0) return MTP_ERR_SHAPE;
+  if (n_rows == 0) return MTP_OK;
+  if (!k_rows || !v_rows || !slots) return MTP_ERR_NULL;
+  const mtp_status sn = check_nested(kv, false);
+  if (sn != MTP_OK) return sn;
+  QuantizeParams p;
+  p.k_rows = k_rows;
+  p.v_rows = v_rows;
+  p.slots = slots;
+  p.kv = *kv;
+  p.n = n_rows;
+  p.Hkv = shape->Hkv;
+  p.D = shape->D;
+  p.dtype = shape->dtype;
+  p.num_pages = shape->num_pages;
+  const long waves = (long)n_rows * shape->Hkv * 2;
+  if ((waves + 3) / 4 > 0x7fffffffL) return MTP_ERR_SHAPE;
+  kv_quantize_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream)>>>(p);
+  return launch_status();
+}
+
+mtp_status mtp_kv_commit_nested(const mtp_shape* shape, const void* k_new, const void* v_new,
+                                const int32_t* accept_len, const int32_t* accept_path,
+                                const int32_t* block_table, const int32_t* ctx_lens_in,
+                                int32_t* ctx_lens_out, int32_t skip_root, const mtp_nested_kv* kv,
+                                void* stream) {
+  NestedCommitParams np;
+  // the plain commit's checks, with the planes standing in for the cache
+  mtp_status st = fill_commit(shape, k_new, v_new, accept_len, accept_path, block_table,
+                              ctx_lens_in, ctx_lens_out, skip_root,
+                              kv != nullptr ? kv->k_base : nullptr,
+                              kv != nullptr ? kv->v_base : nullptr, false, np.c);
+  if (st != MTP_OK || shape->B == 0) return st;
+  st = check_nested(kv, false);
+  if (st != MTP_OK) return st;
+  np.kv = *kv;
+  np.Hkv = shape->Hkv;
+  np.D = shape->D;
+  np.dtype = shape->dtype;
+  commit_nested_kernel<<<dim3(shape->B), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(np);
   return launch_status();
 }
 

@@ -24,9 +24,14 @@ DEV_BAD_MASK, DEV_BAD_CTX, DEV_BAD_PAGE, DEV_BAD_ACCEPT = 1, 2, 4, 8
 EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_size",
            "mtp_verify_attn", "mtp_verify_attn_partial", "mtp_verify_attn_combine",
            "mtp_accept", "mtp_accept_hybrid", "mtp_kv_commit", "mtp_accept_commit",
-           "mtp_verify_step", "mtp_get_device_status")
+           "mtp_verify_step", "mtp_kv_quantize", "mtp_kv_commit_nested",
+           "mtp_verify_attn_nested_workspace_size", "mtp_verify_attn_nested",
+           "mtp_verify_attn_nested_partial", "mtp_verify_attn_nested_combine",
+           "mtp_get_device_status")
 _ATTN_FN = {"both": "mtp_verify_attn", "partial": "mtp_verify_attn_partial",
             "combine": "mtp_verify_attn_combine"}
+_NESTED_FN = {"both": "mtp_verify_attn_nested", "partial": "mtp_verify_attn_nested_partial",
+              "combine": "mtp_verify_attn_nested_combine"}
 
 
 class MtpError(RuntimeError):
@@ -42,6 +47,11 @@ class Shape(ctypes.Structure):
                 ("max_ctx_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("seg_lookback", ctypes.c_int32),
                 ("split_tokens", ctypes.c_int32)]
+
+
+class NestedKVStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("k_base", "k_ref", "k_scale",
+                                                "v_base", "v_ref", "v_scale")]
 
 
 _lib = None
@@ -79,6 +89,16 @@ def load() -> ctypes.CDLL:
                                       + [_i32, _vp, _vp, _vp])
     lib.mtp_verify_step.restype = _i32
     lib.mtp_verify_step.argtypes = ([sp] + [_vp] * 10 + [_i32] + [_vp] * 7 + [_i32, _vp, _sz, _vp])
+    npp = ctypes.POINTER(NestedKVStruct)
+    lib.mtp_kv_quantize.restype = _i32
+    lib.mtp_kv_quantize.argtypes = [sp, _vp, _vp, _i32, _vp, npp, _vp]
+    lib.mtp_kv_commit_nested.restype = _i32
+    lib.mtp_kv_commit_nested.argtypes = [sp] + [_vp] * 7 + [_i32, npp, _vp]
+    lib.mtp_verify_attn_nested_workspace_size.restype = _i32
+    lib.mtp_verify_attn_nested_workspace_size.argtypes = [sp, ctypes.POINTER(_sz)]
+    for fn in _NESTED_FN.values():
+        getattr(lib, fn).restype = _i32
+        getattr(lib, fn).argtypes = [sp, _vp, npp] + [_vp] * 6 + [_i32, _vp, _vp, _vp, _sz, _vp]
     lib.mtp_get_device_status.restype = _i32
     lib.mtp_get_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i32]
     if lib.mtp_abi_version() != 1:
@@ -324,3 +344,107 @@ def device_status(clear: bool = True) -> int:
 
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
+
+
+# ----------------------------------------------------------------------------
+# nested KV4 / KV8 cache
+# ----------------------------------------------------------------------------
+
+class NestedKV:
+    """The six planes of a nested cache as torch tensors (allocation only):
+    base / ref [num_pages, Hkv, 16, D/2] uint8 and scale [num_pages, Hkv, 16]
+    fp32, for K and for V."""
+
+    def __init__(self, num_pages: int, Hkv: int, D: int, device="cuda", with_ref: bool = True):
+        def codes():
+            return torch.zeros((num_pages, Hkv, 16, D // 2), dtype=torch.uint8, device=device)
+        self.num_pages, self.Hkv, self.D = num_pages, Hkv, D
+        self.k_base, self.v_base = codes(), codes()
+        self.k_ref = codes() if with_ref else None
+        self.v_ref = codes() if with_ref else None
+        self.k_scale = torch.zeros((num_pages, Hkv, 16), dtype=torch.float32, device=device)
+        self.v_scale = torch.zeros((num_pages, Hkv, 16), dtype=torch.float32, device=device)
+
+    def c(self) -> NestedKVStruct:
+        return NestedKVStruct(*(_ptr(t) for t in (self.k_base, self.k_ref, self.k_scale,
+                                                    self.v_base, self.v_ref, self.v_scale)))
+
+    def planes(self, which: str) -> dict:
+        """Host numpy copies of the K ("k") or V ("v") planes."""
+        return {"base": getattr(self, which + "_base").cpu().numpy(),
+                "ref": getattr(self, which + "_ref").cpu().numpy(),
+                "scale": getattr(self, which + "_scale").cpu().numpy()}
+
+
+def kv_quantize(k_rows, v_rows, slots, kv: NestedKV, *, stream=None):
+    """Quantizes rows [n, Hkv, D] (fp32 or bf16) into slots [n] (page * 16 + slot)."""
+    lib = load()
+    n, Hkv, D = k_rows.shape
+    cs = Shape(0, 1, Hkv, Hkv, D, 16, kv.num_pages, 0, 0, _dtype_code(k_rows), 0.0, -1, 0)
+    ckv = kv.c()
+    _check("mtp_kv_quantize", lib.mtp_kv_quantize(
+        ctypes.byref(cs), _ptr(k_rows), _ptr(v_rows), n, _ptr(slots), ctypes.byref(ckv),
+        _stream(stream)))
+
+
+def kv_quantize_cache(k_cache, v_cache, kv: NestedKV, *, stream=None):
+    """Quantizes every slot of a [pages, 16, Hkv, D] cache (prefill helper)."""
+    pages, _, Hkv, D = k_cache.shape
+    slots = torch.arange(pages * 16, dtype=torch.int32, device=k_cache.device)
+    kv_quantize(k_cache.reshape(pages * 16, Hkv, D), v_cache.reshape(pages * 16, Hkv, D), slots,
+                kv, stream=stream)
+
+
+def kv_commit_nested(k_new, v_new, accept_len, accept_path, block_table, ctx_lens_in,
+                     kv: NestedKV, *, ctx_lens_out=None, skip_root=False, stream=None):
+    """Quantizing commit into a nested cache; returns ctx_lens_out."""
+    lib = load()
+    if ctx_lens_out is None:
+        ctx_lens_out = torch.empty_like(ctx_lens_in)
+    B, W, Hkv, D = k_new.shape
+    cs = Shape(B, W, Hkv, Hkv, D, 16, kv.num_pages, block_table.shape[1], 0, _dtype_code(k_new),
+               0.0, -1, 0)
+    ckv = kv.c()
+    _check("mtp_kv_commit_nested", lib.mtp_kv_commit_nested(
+        ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(accept_len), _ptr(accept_path),
+        _ptr(block_table), _ptr(ctx_lens_in), _ptr(ctx_lens_out), int(bool(skip_root)),
+        ctypes.byref(ckv), _stream(stream)))
+    return ctx_lens_out
+
+
+def nested_workspace_bytes(shape: VerifyShape) -> int:
+    n = ctypes.c_size_t(0)
+    cs = shape.c()
+    _check("mtp_verify_attn_nested_workspace_size",
+           load().mtp_verify_attn_nested_workspace_size(ctypes.byref(cs), ctypes.byref(n)))
+    return int(n.value)
+
+
+def verify_attn_nested(q, kv: NestedKV, block_table, ctx_lens, k_new, v_new, mask_kind, mask_ids,
+                       *, kv8_recent=-1, out=None, lse=None, want_lse=True, workspace=None,
+                       shape=None, max_ctx_len=None, scale=0.0, seg_lookback=-1, split_tokens=0,
+                       stream=None, phase="both"):
+    """Verify attention over a nested cache; returns (out, lse).  phase
+    "partial" / "combine" launches only one of the two kernels."""
+    lib = load()
+    B, W, Hq, D = q.shape
+    if shape is None:
+        maxp = block_table.shape[1]
+        shape = VerifyShape(B, W, Hq, kv.Hkv, D, kv.num_pages, maxp,
+                            maxp * 16 if max_ctx_len is None else int(max_ctx_len),
+                            _dtype_code(q), float(scale), int(seg_lookback), int(split_tokens))
+    if out is None:
+        out = torch.empty((B, W, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, W, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(nested_workspace_bytes(shape), 16), dtype=torch.uint8,
+                                device=q.device)
+    cs = shape.c()
+    ckv = kv.c()
+    fn = _NESTED_FN[phase]
+    _check(fn, getattr(lib, fn)(
+        ctypes.byref(cs), _ptr(q), ctypes.byref(ckv), _ptr(block_table), _ptr(ctx_lens),
+        _ptr(k_new), _ptr(v_new), _ptr(mask_kind), _ptr(mask_ids), int(kv8_recent), _ptr(out),
+        _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
