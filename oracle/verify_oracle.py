@@ -522,3 +522,94 @@ def kv_commit_nested(k_planes, v_planes, k_new, v_new, accept_len, accept_path, 
             planes["ref"][page, :, slot] = pack_nibbles(qr)
             planes["scale"][page, :, slot] = sc
     return kp, vp, ctx
+
+
+# ----------------------------------------------------------------------------
+# dynamic token tree (block construction for the next verify step)
+# ----------------------------------------------------------------------------
+#
+# "Efficient Training-Free Multi-Token Prediction via Embedding-Space
+# Probing", §2.C (dynamic tree: expansion by cumulative probability, only the
+# top-1 token of each depth expanded, a fixed block-complexity budget, pruning
+# of consecutive repeated tokens) and §2.D (block = last token + predicted
+# tokens + mask tokens; masks and positions by offsets).  Reading used here:
+#   * inputs: the drafter's probabilities p_d over the vocabulary for depths
+#     d = 1..K (fp32), the last committed token (the root), the block width W
+#     and the number of mask-token rows n_mask; W - 1 - n_mask rows hold
+#     predicted tokens;
+#   * pruning: at depth d a token equal to its parent's token is dropped;
+#   * the top-1 (spine) token s_d of depth d is the most probable remaining
+#     token (smallest id on ties); only spine nodes get children, so every
+#     depth-d candidate is a child of s_{d-1} with cumulative probability
+#     c_{d-1} * p_d(v), c_0 = 1, c_d = c_{d-1} * p_d(s_d) (fp32 products, in
+#     this order: the comparisons are taken in the kernel's precision);
+#   * expansion: best first by cumulative probability (ties: shallower, then
+#     more probable at its depth, then smaller id) while prediction rows remain
+#     and the best candidate reaches min_cum_prob;
+#   * rows: 0 = root (draft = root token, parent -1), then the chosen nodes in
+#     the order chosen (parents always come earlier), then mask-token rows
+#     (draft -1): a chain hanging from the deepest chosen spine node (the
+#     root if none).  depth = the row's distance from the root, the position
+#     offset of the row.
+
+def depth_candidates(p_row, parent_token):
+    """Tokens of one depth, most probable first (smallest id on ties),
+    without the parent's token (no consecutive repeats)."""
+    return sorted((v for v in range(len(p_row)) if v != parent_token),
+                  key=lambda v: (-float(p_row[v]), v))
+
+
+def dynamic_tree(probs, root_token, W, n_mask, min_cum_prob=0.0):
+    """probs [B, K, V] fp32 -> draft_ids, parents, depth [B, W] and n_nodes [B]
+    (root + chosen predicted tokens)."""
+    probs = np.asarray(probs, dtype=np.float32)
+    B, K, V = probs.shape
+    slots = W - 1 - n_mask
+    thr = np.float32(min_cum_prob)
+    draft = np.full((B, W), -1, dtype=np.int64)
+    parent = np.full((B, W), -1, dtype=np.int64)
+    depth = np.zeros((B, W), dtype=np.int64)
+    n_nodes = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        # candidates of every depth, most probable first, without the repeat
+        spine_tok = [int(root_token[b])]
+        c = [np.float32(1.0)]
+        lists = []
+        for d in range(1, K + 1):
+            order = depth_candidates(probs[b, d - 1], spine_tok[d - 1])
+            lists.append(order)
+            spine_tok.append(order[0])
+            c.append(np.float32(c[d - 1] * probs[b, d - 1, order[0]]))
+        # best-first expansion: the frontier holds the next unused candidate
+        # of every depth whose parent (the spine node above) is in the tree
+        draft[b, 0], parent[b, 0], depth[b, 0] = spine_tok[0], -1, 0
+        spine_row = {0: 0}
+        nxt = {1: 0} if K >= 1 else {}
+        rows = 1
+        while rows - 1 < slots and nxt:
+            best = None
+            for d, r in nxt.items():
+                v = lists[d - 1][r]
+                cp = np.float32(c[d - 1] * probs[b, d - 1, v])
+                key = (-float(cp), d, r)
+                if best is None or key < best[0]:
+                    best = (key, d, r, v, cp)
+            _, d, r, v, cp = best
+            if cp < thr:
+                break
+            draft[b, rows], parent[b, rows], depth[b, rows] = v, spine_row[d - 1], d
+            if r == 0:  # the spine node of depth d: its children become candidates
+                spine_row[d] = rows
+                if d + 1 <= K:
+                    nxt[d + 1] = 0
+            rows += 1
+            if r + 1 < len(lists[d - 1]):
+                nxt[d] = r + 1
+            else:
+                del nxt[d]
+        n_nodes[b] = rows
+        tail = spine_row[max(spine_row)]
+        for i in range(rows, W):
+            draft[b, i], parent[b, i], depth[b, i] = -1, tail, depth[b, tail] + 1
+            tail = i
+    return draft, parent, depth, n_nodes

@@ -14,6 +14,7 @@ from oracle import verify_oracle as O
 from tests import test_oracle_hybrid as H
 from tests import test_oracle_nested as N
 from tests import test_oracle_pins as P
+from tests import test_oracle_tree as T
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -159,6 +160,24 @@ def _recent_window_off_by_one(*args, kv8_recent=-1, _orig=O.verify_attention_nes
     return _orig(*args, kv8_recent=kv8_recent + 1 if kv8_recent >= 0 else kv8_recent, **kw)
 
 
+def _candidates_unpruned(p_row, parent_token):
+    return sorted(range(len(p_row)), key=lambda v: (-float(p_row[v]), v))
+
+
+def _candidates_ties_to_larger(p_row, parent_token):
+    return sorted((v for v in range(len(p_row)) if v != parent_token),
+                  key=lambda v: (-float(p_row[v]), -v))
+
+
+def _mask_rows_from_root(probs, root_token, W, n_mask, min_cum_prob=0.0, _orig=O.dynamic_tree):
+    d, par, dep, n = _orig(probs, root_token, W, n_mask, min_cum_prob)
+    for b in range(len(n)):
+        tail = 0
+        for i in range(int(n[b]), W):
+            par[b, i], dep[b, i], tail = tail, dep[b, tail] + 1, i
+    return d, par, dep, n
+
+
 MUTANTS = [
     ("block_visibility", _tree_vis_without_self, [(P.test_tree_visibility_is_ancestor_closure, 3),
                                                   (P.test_tree_golden_fixture,)]),
@@ -186,6 +205,9 @@ MUTANTS = [
     ("dequantize_nested", _kv8_without_refinement,
      [(N.test_golden_rows,), (N.test_grid_exact_cache_reduces_to_dense_attention, "chain")]),
     ("dequantize_nested", _refinement_grid_eighth, [(N.test_golden_rows,)]),
+    ("depth_candidates", _candidates_unpruned, [(T.test_golden_tree,)]),
+    ("depth_candidates", _candidates_ties_to_larger, [(T.test_ties_go_to_the_smaller_token,)]),
+    ("dynamic_tree", _mask_rows_from_root, [(T.test_golden_tree,)]),
     ("verify_attention_nested", _recent_window_off_by_one,
      [(N.test_recent_window_reads_kv8_only_for_the_newest_tokens,)]),
 ]
