@@ -276,6 +276,36 @@ def bench_nested_attn(wl: I.Workload, inp: dict, args) -> int:
     return 0
 
 
+def bench_tree(wl: I.Workload, args) -> int:
+    """The dynamic tree builder on its own: B sequences of the workload, K = 8
+    probed depths over its vocabulary, a block of its width with 4 mask rows.
+    Algorithmic bytes: the probability rows read plus the int32 outputs."""
+    K, n_mask = 8, min(4, wl.W - 1)
+    tin = I.make_tree_inputs(wl.B, K, wl.vocab, I.workload_seed(wl.name), device="cuda")
+
+    def launch():
+        lib.build_tree(tin["probs"], tin["root"], wl.W, n_mask)
+
+    ms = timed_graph(launch, args.steps, args.warmup)
+    nbytes = wl.B * (K * wl.vocab * 4 + 4 + wl.W * 12 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "dynamic tree builds/s at 1 GPU", "value": round(1e3 / ms, 1),
+        "unit": "launches/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded heavy-tailed drafter probabilities)",
+        "config": {"workload": wl.name, "B": wl.B, "K": K, "V": wl.vocab, "W": wl.W,
+                   "n_mask": n_mask},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "tree_build_kernel", "kernel_us": round(ms * 1e3, 3),
+                     "algorithmic_bytes": nbytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,10 +321,12 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only time a plain device copy of MB megabytes (HBM reference and "
                          "the FETCH_SIZE/WRITE_SIZE calibration kernel), then exit")
-    ap.add_argument("--kernel", default="step", choices=["step", "accept_hybrid", "nested_attn"],
+    ap.add_argument("--kernel", default="step",
+                    choices=["step", "accept_hybrid", "nested_attn", "tree"],
                     help="step: the whole verify step (default); accept_hybrid: only the "
                          "confidence/hybrid acceptance kernel; nested_attn: verify attention "
-                         "over the nested KV4/KV8 cache")
+                         "over the nested KV4/KV8 cache; tree: the dynamic tree builder for "
+                         "the workload's B and W (K = 8 probed depths, 4 mask rows)")
     ap.add_argument("--kv8-recent", type=int, default=-1,
                     help="nested_attn: -1 all KV8, 0 all KV4, N the N newest tokens in KV8")
     ap.add_argument("--tau", type=float, default=0.9)
@@ -344,6 +376,8 @@ def main() -> int:
         return bench_accept_hybrid(wl, inp, args)
     if args.kernel == "nested_attn":
         return bench_nested_attn(wl, inp, args)
+    if args.kernel == "tree":
+        return bench_tree(wl, args)
     host = inp["host"]
     ctx = host["ctx_lens"]
     nbytes = algorithmic_bytes(wl, ctx)

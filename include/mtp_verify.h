@@ -331,6 +331,36 @@ mtp_status mtp_verify_attn_nested_combine(const mtp_shape* shape, const void* q,
                                           float* out, float* lse, void* workspace,
                                           size_t workspace_bytes, void* stream);
 
+/* Dynamic token tree for the next block ("Efficient Training-Free Multi-Token
+ * Prediction via Embedding-Space Probing", Sec. 2.C: expansion by cumulative
+ * probability, only the top-1 token of each depth expanded, a fixed budget,
+ * consecutive repeated tokens pruned; Sec. 2.D: block = last token +
+ * predicted tokens + mask tokens, positions by offsets).
+ *
+ *   probs      [B, K, V] fp32 (device): the drafter's probabilities for
+ *              depths 1..K (finite, >= 0); K in [1, 64]
+ *   root_token [B] int32: the last committed token (block row 0)
+ *   W, n_mask  block width (1..64) and mask-token rows (0..W-1); W - 1 -
+ *              n_mask rows hold predicted tokens
+ *   outputs    draft_ids, parents, depth [B, W] int32; n_nodes [B] int32
+ *
+ * At depth d the parent's token is dropped; the most probable remaining
+ * token (smallest id on ties) is the depth's top-1 node, the parent of every
+ * depth-(d+1) candidate; a candidate's cumulative probability is
+ * c_{d-1} * p_d(v), c_0 = 1, c_d = c_{d-1} * p_d(top-1) (fp32 products in this
+ * order).  Nodes are chosen best first (ties: shallower, then more probable
+ * at its depth, then smaller id) while predicted rows remain and the best
+ * reaches min_cum_prob (NaN rejected).  Row 0 = root (draft = root token,
+ * parent -1), then the chosen nodes in the order chosen, then mask-token rows
+ * (draft -1) chained from the deepest chosen top-1 node.  parents is a valid
+ * TREE mask description and depth the position offset of each row;
+ * n_nodes = 1 + chosen nodes.  Cost grows with V (each list is built by a
+ * wave; V <= 1024 is held in registers). */
+mtp_status mtp_build_tree(int32_t B, int32_t K, int32_t V, int32_t W, int32_t n_mask,
+                          const float* probs, const int32_t* root_token, float min_cum_prob,
+                          int32_t* draft_ids, int32_t* parents, int32_t* depth,
+                          int32_t* n_nodes, void* stream);
+
 /* Reads (and with clear != 0 resets) the current device's sticky status word
  * into *bits.  Synchronous: waits for all work on the device. */
 mtp_status mtp_get_device_status(uint32_t* bits, int32_t clear);

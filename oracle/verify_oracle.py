@@ -577,6 +577,8 @@ def dynamic_tree(probs, root_token, W, n_mask, min_cum_prob=0.0):
         lists = []
         for d in range(1, K + 1):
             order = depth_candidates(probs[b, d - 1], spine_tok[d - 1])
+            if not order:  # a one-token vocabulary: nothing below the root
+                break
             lists.append(order)
             spine_tok.append(order[0])
             c.append(np.float32(c[d - 1] * probs[b, d - 1, order[0]]))
@@ -584,7 +586,7 @@ def dynamic_tree(probs, root_token, W, n_mask, min_cum_prob=0.0):
         # of every depth whose parent (the spine node above) is in the tree
         draft[b, 0], parent[b, 0], depth[b, 0] = spine_tok[0], -1, 0
         spine_row = {0: 0}
-        nxt = {1: 0} if K >= 1 else {}
+        nxt = {1: 0} if lists else {}
         rows = 1
         while rows - 1 < slots and nxt:
             best = None
@@ -600,7 +602,7 @@ def dynamic_tree(probs, root_token, W, n_mask, min_cum_prob=0.0):
             draft[b, rows], parent[b, rows], depth[b, rows] = v, spine_row[d - 1], d
             if r == 0:  # the spine node of depth d: its children become candidates
                 spine_row[d] = rows
-                if d + 1 <= K:
+                if d + 1 <= len(lists):
                     nxt[d + 1] = 0
             rows += 1
             if r + 1 < len(lists[d - 1]):

@@ -16,6 +16,7 @@
 #include "common.hpp"
 #include "hybrid.hpp"
 #include "nested.hpp"
+#include "tree.hpp"
 #include "attn_nested_lds.hpp"
 #include "mtp_verify.h"
 
@@ -636,6 +637,33 @@ mtp_status mtp_kv_commit_nested(const mtp_shape* shape, const void* k_new, const
   np.D = shape->D;
   np.dtype = shape->dtype;
   commit_nested_kernel<<<dim3(shape->B), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(np);
+  return launch_status();
+}
+
+mtp_status mtp_build_tree(int32_t B, int32_t K, int32_t V, int32_t W, int32_t n_mask,
+                          const float* probs, const int32_t* root_token, float min_cum_prob,
+                          int32_t* draft_ids, int32_t* parents, int32_t* depth,
+                          int32_t* n_nodes, void* stream) {
+  if (B < 0 || B > 65535 || K < 1 || K > kTreeMaxK || V < 1 || W < 1 || W > MTP_MAX_W ||
+      n_mask < 0 || n_mask > W - 1 || min_cum_prob != min_cum_prob)
+    return MTP_ERR_SHAPE;
+  if (B == 0) return MTP_OK;
+  if (!probs || !root_token || !draft_ids || !parents || !depth || !n_nodes) return MTP_ERR_NULL;
+  TreeParams p;
+  p.probs = probs;
+  p.root = root_token;
+  p.draft = draft_ids;
+  p.parent = parents;
+  p.depth = depth;
+  p.n_nodes = n_nodes;
+  p.min_cum_prob = min_cum_prob;
+  p.B = B;
+  p.K = K;
+  p.V = V;
+  p.W = W;
+  p.n_mask = n_mask;
+  const int threads = kWave * std::min(16, K);
+  tree_build_kernel<<<dim3(B), dim3(threads), 0, static_cast<hipStream_t>(stream)>>>(p);
   return launch_status();
 }
 

@@ -312,3 +312,15 @@ def kv_bytes(wl: Workload, ctx_lens: np.ndarray) -> int:
     """Committed K+V bytes one verify step must read (the headline numerator)."""
     elem = 4 if wl.dtype == "f32" else 2
     return int(np.sum(ctx_lens.astype(np.int64))) * wl.Hkv * wl.D * 2 * elem
+
+
+def make_tree_inputs(B: int, K: int, V: int, seed: int, peak: float = 8.0, device="cpu") -> dict:
+    """Drafter probabilities for the tree builder: per (sequence, depth) a
+    heavy-tailed distribution (uniform draws to the power `peak`, normalised
+    in fp32), and a root token per sequence."""
+    rng = np.random.default_rng(seed)
+    w = rng.random((B, K, V)) ** peak
+    probs = (w / w.sum(axis=-1, keepdims=True)).astype(np.float32)
+    root = rng.integers(0, V, size=B).astype(np.int32)
+    return dict(probs=torch.from_numpy(probs).to(device), root=torch.from_numpy(root).to(device),
+                host=dict(probs=probs, root=root))
