@@ -306,6 +306,91 @@ def bench_tree(wl: I.Workload, args) -> int:
     return 0
 
 
+def bench_loop(wl: I.Workload, args) -> int:
+    """A device-resident decode loop: N dependent steps (block positions, then
+    the verify step reading the context lengths the previous commit wrote)
+    replayed from one graph (with a reset of the first context buffer at its
+    head), against the same N steps launched eagerly.  Warm cache (the loop
+    rereads one pool)."""
+    N = args.loop_steps
+    wl = wl.scaled(commit_steps=N + 1)
+    seed = I.workload_seed(wl.name)
+    base = I.make_inputs(wl, seed, device="cuda")
+    steps = [I.make_inputs(wl, seed + 1000 * (k + 1), device="cuda") for k in range(N)]
+    bt, kc, vc = base["block_table"], base["k_cache"], base["v_cache"]
+    ctx0 = base["ctx_lens"].clone()
+    ctx = [base["ctx_lens"].clone(), torch.empty_like(ctx0)]
+    mc = int(base["host"]["ctx_lens"].max()) + N * wl.W
+    shape = lib.shape_of(steps[0]["q"], kc, bt, max_ctx_len=mc, scale=base["scale"],
+                         seg_lookback=wl.seg_lookback)
+    ws = torch.empty(max(lib.workspace_bytes(shape), 16), dtype=torch.uint8, device="cuda")
+    B, W, Hq, D = steps[0]["q"].shape
+    out = torch.empty((B, W, Hq, D), device="cuda")
+    lse = torch.empty((B, W, Hq), device="cuda")
+    alen = torch.empty(B, dtype=torch.int32, device="cuda")
+    apath = torch.empty((B, W), dtype=torch.int32, device="cuda")
+    bonus = torch.empty(B, dtype=torch.int32, device="cuda")
+    pos = torch.empty((B, W), dtype=torch.int32, device="cuda")
+
+    def loop():
+        ctx[0].copy_(ctx0)
+        for k in range(N):
+            s = steps[k]
+            cin, cout = ctx[k % 2], ctx[(k + 1) % 2]
+            lib.block_positions(cin, s["mask_kind"], s["mask_ids"], positions=pos)
+            lib.verify_step(s["q"], kc, vc, bt, cin, s["k_new"], s["v_new"], s["mask_kind"],
+                            s["mask_ids"], s["logits"], s["draft_ids"], out=out, lse=lse,
+                            accept_len=alen, accept_path=apath, bonus_id=bonus,
+                            ctx_lens_out=cout, workspace=ws, shape=shape)
+
+    loop()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // N)
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        loop()
+    z.record()
+    torch.cuda.synchronize()
+    eager_ms = a.elapsed_time(z) / (reps * N)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            loop()
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup // N)):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    z.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    graph_ms = a.elapsed_time(z) / (reps * N)
+    if lib.device_status(clear=True) != 0:
+        print("bench.py: the device reported a data error", file=sys.stderr)
+        return 3
+    kvb = algorithmic_bytes(wl, base["host"]["ctx_lens"])["kv"]
+    rec = {
+        "metric": "device-resident decode loop: verify steps/s at 1 GPU",
+        "value": round(1e3 / graph_ms, 1), "unit": "steps/s", "n_gpus": 1,
+        "steps": reps * N, "warmup": args.warmup, "ms_per_step": round(graph_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; a different block per step, one pool)",
+        "config": {"workload": wl.name, "B": wl.B, "W": wl.W, "loop_steps": N, "cache": "warm"},
+        "eager_ms_per_step": round(eager_ms, 5),
+        "graph_wall_ms_per_step": round((t1 - t0) * 1e3 / (reps * N), 5),
+        "kv_GBs_first_step": round(kvb / (graph_ms * 1e-3) / 1e9, 1),
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,11 +407,14 @@ def main() -> int:
                     help="only time a plain device copy of MB megabytes (HBM reference and "
                          "the FETCH_SIZE/WRITE_SIZE calibration kernel), then exit")
     ap.add_argument("--kernel", default="step",
-                    choices=["step", "accept_hybrid", "nested_attn", "tree"],
+                    choices=["step", "accept_hybrid", "nested_attn", "tree", "loop"],
                     help="step: the whole verify step (default); accept_hybrid: only the "
                          "confidence/hybrid acceptance kernel; nested_attn: verify attention "
                          "over the nested KV4/KV8 cache; tree: the dynamic tree builder for "
-                         "the workload's B and W (K = 8 probed depths, 4 mask rows)")
+                         "the workload's B and W (K = 8 probed depths, 4 mask rows); loop: "
+                         "--loop-steps dependent steps (positions + verify step, each step's "
+                         "context lengths from the previous commit) in one graph vs eager")
+    ap.add_argument("--loop-steps", type=int, default=8)
     ap.add_argument("--kv8-recent", type=int, default=-1,
                     help="nested_attn: -1 all KV8, 0 all KV4, N the N newest tokens in KV8")
     ap.add_argument("--tau", type=float, default=0.9)
@@ -378,6 +466,8 @@ def main() -> int:
         return bench_nested_attn(wl, inp, args)
     if args.kernel == "tree":
         return bench_tree(wl, args)
+    if args.kernel == "loop":
+        return bench_loop(wl, args)
     host = inp["host"]
     ctx = host["ctx_lens"]
     nbytes = algorithmic_bytes(wl, ctx)

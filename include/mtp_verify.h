@@ -361,6 +361,21 @@ mtp_status mtp_build_tree(int32_t B, int32_t K, int32_t V, int32_t W, int32_t n_
                           int32_t* draft_ids, int32_t* parents, int32_t* depth,
                           int32_t* n_nodes, void* stream);
 
+/* Positions of the block rows for the verifier's inputs, prepared on the
+ * device ("BitMTP" Sec. 3.4 M3: verifier inputs follow the materialized KV
+ * boundary and are prepared before the host reads the acceptance; "Efficient
+ * Training-Free Multi-Token Prediction via Embedding-Space Probing" Sec. 2.D:
+ * position indices by offsets).  Uses B and W of `shape`.
+ *   positions [B, W] int32 (written): ctx_lens[b] + the row's depth below the
+ *   anchor: the row index for CHAIN and SEGMENT blocks, the number of
+ *   ancestors for TREE blocks.  A malformed mask writes -1 for the sequence
+ *   (MTP_DEV_BAD_MASK).
+ * With ctx_lens = the previous step's ctx_lens_out this needs no host
+ * round trip between steps. */
+mtp_status mtp_block_positions(const mtp_shape* shape, const int32_t* ctx_lens,
+                               const uint8_t* mask_kind, const int32_t* mask_ids,
+                               int32_t* positions, void* stream);
+
 /* Reads (and with clear != 0 resets) the current device's sticky status word
  * into *bits.  Synchronous: waits for all work on the device. */
 mtp_status mtp_get_device_status(uint32_t* bits, int32_t clear);

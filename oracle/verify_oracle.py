@@ -615,3 +615,34 @@ def dynamic_tree(probs, root_token, W, n_mask, min_cum_prob=0.0):
             draft[b, i], parent[b, i], depth[b, i] = -1, tail, depth[b, tail] + 1
             tail = i
     return draft, parent, depth, n_nodes
+
+
+# ----------------------------------------------------------------------------
+# block positions (verifier-input preparation on the device)
+# ----------------------------------------------------------------------------
+
+def block_positions(ctx_lens, mask_kind, mask_ids):
+    """[B, W] position of every block row: the committed length plus the
+    row's depth below the anchor ("BitMTP" §3.4 M3: the verifier's positions
+    follow the materialized KV boundary; "Efficient Training-Free Multi-Token
+    Prediction via Embedding-Space Probing" §2.D: position indices by
+    offsets).  Chain and segment blocks are sequential (depth = row index);
+    a tree row's depth is its number of ancestors.  A malformed mask gives -1
+    for the whole sequence."""
+    mask_ids = np.asarray(mask_ids)
+    B, W = mask_ids.shape
+    pos = np.full((B, W), -1, dtype=np.int64)
+    for b in range(B):
+        kind, ids = int(mask_kind[b]), mask_ids[b]
+        if not mask_is_valid(kind, ids):
+            continue
+        for i in range(W):
+            depth, j = 0, i
+            if kind == TREE:
+                while j > 0:
+                    j = int(ids[j])
+                    depth += 1
+            else:
+                depth = i
+            pos[b, i] = int(ctx_lens[b]) + depth
+    return pos

@@ -377,6 +377,24 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
   block_commit<false>(p, b, commit_prefetch(p, b), 0, nullptr, s_src, s_dst, s_meta);
 }
 
+// Positions of the block rows: ctx_lens[b] + the row's depth below the
+// anchor (chain / segment: the row index; tree: ancestors counted from the
+// ancestor-or-self bit row).  One wave per sequence; a malformed mask gives
+// -1 for the sequence and sets the status bit.
+__global__ __launch_bounds__(256) void positions_kernel(const int32_t* ctx_lens, const uint8_t* mask_kind,
+                                                        const int32_t* mask_ids, int32_t* positions,
+                                                        int B, int W) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const int lane = threadIdx.x & 63;
+  const int kind = mask_kind[b];
+  const int id = lane < W ? mask_ids[(size_t)b * W + lane] : 0;
+  const int L = ctx_lens[b];
+  const NodeTree t = node_tree(kind, id, W);
+  if (lane < W) positions[(size_t)b * W + lane] = t.ok ? L + __popcll(t.anc) - 1 : -1;
+  if (!t.ok && lane == 0) raise_status(MTP_DEV_BAD_MASK);
+}
+
 // LDS scratch of one fused acceptance + commit, in ints.
 constexpr int kAcceptScratchInts = 4 * MTP_MAX_W + 2;
 

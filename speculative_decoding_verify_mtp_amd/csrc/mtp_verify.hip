@@ -667,6 +667,20 @@ mtp_status mtp_build_tree(int32_t B, int32_t K, int32_t V, int32_t W, int32_t n_
   return launch_status();
 }
 
+mtp_status mtp_block_positions(const mtp_shape* shape, const int32_t* ctx_lens,
+                               const uint8_t* mask_kind, const int32_t* mask_ids,
+                               int32_t* positions, void* stream) {
+  if (shape == nullptr) return MTP_ERR_NULL;
+  if (shape->B < 0 || shape->B > 65535 * 4 || shape->W < 1 || shape->W > MTP_MAX_W)
+    return MTP_ERR_SHAPE;
+  if (shape->B == 0) return MTP_OK;
+  if (!ctx_lens || !mask_kind || !mask_ids || !positions) return MTP_ERR_NULL;
+  positions_kernel<<<dim3((unsigned)((shape->B + 3) / 4)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream)>>>(ctx_lens, mask_kind, mask_ids, positions,
+                                                         shape->B, shape->W);
+  return launch_status();
+}
+
 mtp_status mtp_get_device_status(uint32_t* bits, int32_t clear) {
   if (bits == nullptr) return MTP_ERR_NULL;
   if (hipDeviceSynchronize() != hipSuccess) return MTP_ERR_HIP;

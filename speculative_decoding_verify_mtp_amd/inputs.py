@@ -74,6 +74,7 @@ class Workload:
     vocab: int = 1000
     mask_token_rows: int = 0  # trailing rows whose draft id is -1 (never accepted)
     conf_p: float = 0.8  # probability that a draft's logit lift is a confident one
+    commit_steps: int = 1  # pages are mapped for this many steps of W committed rows
 
     @property
     def group(self) -> int:
@@ -207,8 +208,9 @@ def make_structure(wl: Workload, seed: int) -> dict:
             ids[b] = random_segments(rng, W, wl.seg_max)
             accept_parent[b] = chain_parents(W)
 
-    # pages: every logical slot up to ctx + W - 1 is mapped (commit workspace)
-    n_pages = [(int(L) + W + PAGE_SIZE - 1) // PAGE_SIZE for L in ctx]
+    # pages: every logical slot up to ctx + commit_steps * W - 1 is mapped
+    # (commit workspace)
+    n_pages = [(int(L) + wl.commit_steps * W + PAGE_SIZE - 1) // PAGE_SIZE for L in ctx]
     pool = int(sum(n_pages)) + wl.spare_pages
     order = rng.permutation(pool).astype(np.int32) if wl.shuffle_pages else \
         np.arange(pool, dtype=np.int32)

@@ -27,7 +27,7 @@ EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_si
            "mtp_verify_step", "mtp_kv_quantize", "mtp_kv_commit_nested",
            "mtp_verify_attn_nested_workspace_size", "mtp_verify_attn_nested",
            "mtp_verify_attn_nested_partial", "mtp_verify_attn_nested_combine",
-           "mtp_build_tree", "mtp_get_device_status")
+           "mtp_build_tree", "mtp_block_positions", "mtp_get_device_status")
 _ATTN_FN = {"both": "mtp_verify_attn", "partial": "mtp_verify_attn_partial",
             "combine": "mtp_verify_attn_combine"}
 _NESTED_FN = {"both": "mtp_verify_attn_nested", "partial": "mtp_verify_attn_nested_partial",
@@ -101,6 +101,8 @@ def load() -> ctypes.CDLL:
         getattr(lib, fn).argtypes = [sp, _vp, npp] + [_vp] * 6 + [_i32, _vp, _vp, _vp, _sz, _vp]
     lib.mtp_build_tree.restype = _i32
     lib.mtp_build_tree.argtypes = [_i32] * 5 + [_vp, _vp, ctypes.c_float] + [_vp] * 4 + [_vp]
+    lib.mtp_block_positions.restype = _i32
+    lib.mtp_block_positions.argtypes = [sp] + [_vp] * 4 + [_vp]
     lib.mtp_get_device_status.restype = _i32
     lib.mtp_get_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i32]
     if lib.mtp_abi_version() != 1:
@@ -465,3 +467,16 @@ def build_tree(probs, root_token, W, n_mask, min_cum_prob=0.0, *, stream=None):
         B, K, V, W, n_mask, _ptr(probs), _ptr(root_token), float(min_cum_prob), _ptr(draft),
         _ptr(parents), _ptr(depth), _ptr(n_nodes), _stream(stream)))
     return draft, parents, depth, n_nodes
+
+
+def block_positions(ctx_lens, mask_kind, mask_ids, *, positions=None, stream=None):
+    """Positions [B, W] int32 of the block rows (ctx_lens + depth)."""
+    lib = load()
+    B, W = mask_ids.shape
+    if positions is None:
+        positions = torch.empty((B, W), dtype=torch.int32, device=mask_ids.device)
+    cs = Shape(B, W, 1, 1, 64, 16, 0, 0, 0, MTP_F32, 0.0, -1, 0)
+    _check("mtp_block_positions", lib.mtp_block_positions(
+        ctypes.byref(cs), _ptr(ctx_lens), _ptr(mask_kind), _ptr(mask_ids),
+        _ptr(positions), _stream(stream)))
+    return positions

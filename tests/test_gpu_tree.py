@@ -70,3 +70,16 @@ def test_tree_output_feeds_the_verify_step():
     ref = O.accept(logits.numpy(), ints(d), kinds.numpy(), ints(par))
     assert all(np.array_equal(ints(a), b) for a, b in zip(got, ref))
     assert lib.device_status(clear=True) == 0
+
+
+@pytest.mark.parametrize("masks", ["chain", "tree", "segment", "mixed"])
+def test_block_positions_match_oracle(masks):
+    banner(f"positions {masks}")
+    wl = I.Workload(name="pos", B=9, Hq=2, Hkv=2, D=64, W=24, dtype="bf16", ctx_lo=0,
+                    ctx_hi=500, masks=masks)
+    inp = I.make_inputs(wl, 3, device="cuda")
+    got = lib.block_positions(inp["ctx_lens"], inp["mask_kind"], inp["mask_ids"])
+    torch.cuda.synchronize()
+    h = inp["host"]
+    assert np.array_equal(ints(got), O.block_positions(h["ctx_lens"], h["mask_kind"],
+                                                        h["mask_ids"]))

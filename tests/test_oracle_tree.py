@@ -109,3 +109,20 @@ def test_ties_go_to_the_smaller_token():
     # have cumulative probability 1/6, ahead of depth 2 (1/36)
     assert list(d[0, 1:6]) == [1, 2, 3, 4, 5]
     assert list(d[0, 6:8]) == [0, 2] and list(par[0, 6:8]) == [1, 1]
+
+
+def test_positions_chain_and_segment_are_sequential():
+    ids = np.array([[-1, 0, 1, 2, 3], [0, 0, 1, 1, 2]])
+    pos = O.block_positions([10, 7], [O.CHAIN, O.SEGMENT], ids)
+    assert pos.tolist() == [[10, 11, 12, 13, 14], [7, 8, 9, 10, 11]]
+
+
+def test_positions_of_a_tree_are_depths_from_the_golden_tree():
+    g = load_golden("dynamic_tree_v5.txt")
+    pos = O.block_positions([100], [O.TREE], np.array([g["parents"]]))
+    assert list(pos[0]) == [100 + d for d in g["depth"]]
+
+
+def test_positions_of_a_malformed_mask_are_minus_one():
+    pos = O.block_positions([5], [O.TREE], np.array([[-1, 0, 2]]))
+    assert np.all(pos == -1)
