@@ -34,8 +34,10 @@ from speculative_decoding_verify_mtp_amd import lib  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bitnet2b_chain"
+# The partial kernels and their launch plan: traffic counters taken on other
+# sources are not reported.
 KERNEL_SOURCES = ["attn_lds.hpp", "attn_mfma.hpp", "attn_stream.hpp", "attn_valu.hpp",
-                  "common.hpp", "mtp_verify.hip"]
+                  "common.hpp", "plan.hpp"]
 
 
 def kernel_source_hash() -> str:
@@ -74,6 +76,66 @@ def traffic_from_profile(workload: str, launch_bytes: int) -> float | None:
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return float(rec["bytes_per_launch"])
+
+
+PARTIAL_KERNELS = ("attn_partial_lds", "attn_partial_stream", "attn_partial_mfma",
+                   "attn_partial_valu")
+
+
+def _median_counter(csv_dir: str, counter: str, match) -> tuple[float, int]:
+    import csv
+    import glob
+    vals = []
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} values for the kernel under {csv_dir}")
+    return float(np.median(vals)), len(vals)
+
+
+def write_traffic(workload: str, ctr_dir: str) -> int:
+    """profiles/traffic_<workload>.json from two rocprofv3 --pmc runs of the
+    bench (FETCH_SIZE, WRITE_SIZE) and the same two counters of the copy
+    calibration kernel, under ctr_dir/{<workload>,copy}_{FETCH_SIZE,WRITE_SIZE}.
+    Runs on the CPU."""
+    is_partial = lambda name: any(k in name for k in PARTIAL_KERNELS)  # noqa: E731
+    is_copy = lambda name: "copyBuffer" in name  # the runtime's device-to-device copy  # noqa: E731
+    fetch, nf = _median_counter(os.path.join(ctr_dir, f"{workload}_FETCH_SIZE"), "FETCH_SIZE",
+                                is_partial)
+    write, nw = _median_counter(os.path.join(ctr_dir, f"{workload}_WRITE_SIZE"), "WRITE_SIZE",
+                                is_partial)
+    cf, _ = _median_counter(os.path.join(ctr_dir, "copy_FETCH_SIZE"), "FETCH_SIZE", is_copy)
+    cw, _ = _median_counter(os.path.join(ctr_dir, "copy_WRITE_SIZE"), "WRITE_SIZE", is_copy)
+    copy_kib = 512e6 / 1024
+    ff, fw = copy_kib / cf, copy_kib / cw
+    steps = "--steps 3 --warmup 1" if workload == "ragged_batch" else "--steps 100 --warmup 2"
+    rec = {
+        "workload": workload, "kernel": "partial kernel of the step",
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
+        "dispatches": [nf, nw],
+        "copy_calibration": {"bytes": 512000000, "fetch_size_kib": cf, "write_size_kib": cw,
+                             "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
+        "fetch_bytes_per_launch": int(fetch * 1024 * ff),
+        "write_bytes_per_launch": int(write * 1024 * fw),
+        "bytes_per_launch": int(fetch * 1024 * ff + write * 1024 * fw),
+        "commands": [
+            f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d {ctr_dir}/{t}_{c} -o run "
+            f"-- python bench.py " + (f"--workload {workload} {steps} --no-cpu-baseline"
+                                      if t == workload else "--copy-calibration 512")
+            for t in (workload, "copy") for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
+            f"python bench.py --write-traffic {workload} --ctr-dir {ctr_dir}"],
+        "note": "medians over dispatches of the partial kernel; the copy kernel moves 512 MB "
+                "each way, so factor = 500000 KiB / counter reading",
+    }
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"wrote": f"profiles/traffic_{workload}.json",
+                      "bytes_per_launch": rec["bytes_per_launch"]}))
+    return 0
 
 
 def cpu_baseline(wl: I.Workload, seed: int, budget_s: float) -> dict:
@@ -419,9 +481,15 @@ def main() -> int:
                     help="nested_attn: -1 all KV8, 0 all KV4, N the N newest tokens in KV8")
     ap.add_argument("--tau", type=float, default=0.9)
     ap.add_argument("--min-prefix", type=int, default=2)
+    ap.add_argument("--write-traffic", metavar="WORKLOAD", default=None,
+                    help="only write profiles/traffic_WORKLOAD.json from rocprofv3 counter "
+                         "CSVs under --ctr-dir (no GPU needed), then exit")
+    ap.add_argument("--ctr-dir", default="gpurun_out/ctr")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.write_traffic:
+        return write_traffic(args.write_traffic, args.ctr_dir)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the verify step is measured on one "

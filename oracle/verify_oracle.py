@@ -51,7 +51,14 @@ What it computes, step by step, in the notation of the pages:
   (BitMTP §3.3 hybrid decoding; Multi-Byte Prediction §3.1 byte acceptance).
 
 * Nested KV4 / KV8 cache (``quantize_nested``, ``verify_attention_nested``,
-  ``kv_commit_nested``): BitNest §3.4 / §A.2, see the section at the end.
+  ``kv_commit_nested``): BitNest §3.4 / §A.2, see its section below.
+
+* Dynamic token tree (``dynamic_tree``): the next block built from the
+  drafter's probabilities ("Efficient Training-Free Multi-Token Prediction
+  via Embedding-Space Probing" §2.C-D), see its section below.
+
+* Block positions (``block_positions``): committed length + the row's depth
+  (BitMTP §3.4 M3; Embedding-Space Probing §2.D).
 
 * Commit (``kv_commit``).  The K/V rows of the accepted path, root first, are
   copied to logical positions L, L+1, ..., L+a; rejected rows are never

@@ -17,146 +17,13 @@
 #include "hybrid.hpp"
 #include "nested.hpp"
 #include "tree.hpp"
+#include "plan.hpp"
 #include "attn_nested_lds.hpp"
 #include "mtp_verify.h"
 
 namespace {
 
 using namespace mtpv;
-
-// Committed tokens per split when the caller does not fix it: enough work
-// items to fill 256 CUs several times over (1024 workgroups of the LDS kernel,
-// 2048 single-wave items otherwise), no longer than 2048 tokens, and at least
-// twice the rows of an item (the partial a split writes, rows x (D+2) x 4
-// bytes, then stays below half of the K/V it reads, split x 4D bytes).
-constexpr long kTargetWorkgroups = 1024;
-constexpr long kTargetWaves = 2048;
-constexpr int kMinSplit = 64;
-constexpr int kMaxSplit = 2048;
-
-enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3, kMfmaNested = 4 };
-
-// Stream kernel: persistent grid sized for gfx950's 256 CUs (two workgroups
-// per CU at one row tile per wave, one at two), each workgroup streaming at
-// least kMinStreamStages stages.
-constexpr int kCUs = 256;
-constexpr long kMinStreamStages = 2;
-// A handful of sequences is balanced by the split plan already, and the
-// stream kernel's per-workgroup set-up would dominate their short ranges.
-constexpr int kStreamMinB = 8;
-
-struct Plan {
-  Kernel kernel;   // VALU (fp32, or < 16 rows), MFMA with direct loads (D=64), MFMA + LDS ring (D=128)
-  bool mfma;       // bf16 with >= 16 rows per KV head
-  int g, R;        // group size, rows per KV head (W * g)
-  int RB;          // MFMA row tiles per wave (1, 2 or 4)
-  int NR;          // waves per workgroup (LDS kernel; 1 wave per item otherwise)
-  int nRB;         // row blocks (MFMA) or row chunks (VALU) per KV head
-  int S;           // committed tokens per split
-  int max_splits;  // splits of the longest context
-  int G;           // stream kernel: workgroups
-  int nts, nseg, rows_block;
-  size_t acc_bytes, ml_offset, ml_bytes, seg_offset, seg_bytes;
-};
-
-mtp_status check_shape(const mtp_shape* s) {
-  if (s == nullptr) return MTP_ERR_NULL;
-  if (s->B < 0 || s->B > 65535) return MTP_ERR_SHAPE;
-  if (s->W < 1 || s->W > MTP_MAX_W) return MTP_ERR_SHAPE;
-  if (s->Hkv < 1 || s->Hq < 1 || s->Hq % s->Hkv != 0) return MTP_ERR_SHAPE;
-  if (s->num_pages < 0 || s->max_pages_per_seq < 0 || s->max_ctx_len < 0) return MTP_ERR_SHAPE;
-  if ((int64_t)s->max_ctx_len > (int64_t)s->max_pages_per_seq * MTP_PAGE_SIZE) return MTP_ERR_SHAPE;
-  if (s->max_ctx_len > 0 && s->num_pages < 1) return MTP_ERR_SHAPE;  // committed keys need pages
-  if (s->seg_lookback < -1) return MTP_ERR_SHAPE;
-  if (s->split_tokens < 0 || s->split_tokens % 32 != 0 || s->split_tokens > kMaxSplit)
-    return MTP_ERR_SHAPE;
-  if (!(s->scale >= 0.f) || isinf(s->scale)) return MTP_ERR_SHAPE;
-  if (s->page_size != MTP_PAGE_SIZE) return MTP_ERR_UNSUPPORTED;
-  if (s->D != 64 && s->D != 128) return MTP_ERR_UNSUPPORTED;
-  if (s->dtype != MTP_F32 && s->dtype != MTP_BF16) return MTP_ERR_UNSUPPORTED;
-  return MTP_OK;
-}
-
-int pow2_ceil(long x) {
-  int p = 1;
-  while (p < x && p < (1 << 30)) p <<= 1;
-  return p;
-}
-
-// `nested`: the plan of the nested-cache kernel (bf16, D = 128, LDS ring):
-// workgroups shaped as for the bf16 LDS kernel (fewer rows than a tile are
-// padded to one).
-Plan make_plan(const mtp_shape& s, bool nested = false) {
-  Plan pl;
-  pl.g = s.Hq / s.Hkv;
-  pl.R = s.W * pl.g;
-  pl.mfma = nested || (s.dtype == MTP_BF16 && pl.R >= 16);
-  pl.NR = 1;
-  const int tiles = (pl.R + 15) / 16;
-  if (nested) {
-    pl.kernel = kMfmaNested;
-    pl.NR = tiles >= 3 ? 4 : tiles;
-    const int per = (tiles + pl.NR - 1) / pl.NR;
-    pl.RB = per >= 2 ? 2 : 1;
-    pl.nRB = (tiles + pl.NR * pl.RB - 1) / (pl.NR * pl.RB);
-  } else if (pl.mfma && s.D == 128) {
-    // One workgroup of NR waves shares each K/V stage; wave w owns RB row
-    // tiles.  Up to 4 waves x 2 tiles = 128 rows per row block.
-    pl.kernel = kMfmaLds;
-    pl.NR = tiles >= 3 ? 4 : tiles;
-    const int per = (tiles + pl.NR - 1) / pl.NR;
-    pl.RB = per >= 2 ? 2 : 1;
-    pl.nRB = (tiles + pl.NR * pl.RB - 1) / (pl.NR * pl.RB);
-  } else if (pl.mfma) {
-    // Row tiles per wave: 1, 2 or 4 (a third tile is padded to four so the
-    // K/V stream is still read once).
-    pl.kernel = kMfmaDirect;
-    pl.RB = tiles >= 3 ? 4 : tiles;
-    pl.nRB = (tiles + pl.RB - 1) / pl.RB;
-  } else {
-    pl.kernel = kValu;
-    pl.RB = 0;
-    pl.nRB = (pl.R + kValuRows - 1) / kValuRows;
-  }
-  if (s.split_tokens > 0) {
-    pl.S = s.split_tokens;
-  } else {
-    const bool wg = pl.kernel == kMfmaLds || pl.kernel == kMfmaNested;
-    const long target = wg ? kTargetWorkgroups : kTargetWaves;
-    const int rows_item = wg ? 16 * pl.NR * pl.RB : pl.kernel == kMfmaDirect ? 16 * pl.RB : kValuRows;
-    const long work = (long)s.B * s.Hkv * pl.nRB * (long)(s.max_ctx_len > 0 ? s.max_ctx_len : 1);
-    int S = pow2_ceil((work + target - 1) / target);
-    const int floor_rows = pow2_ceil(2L * rows_item);
-    S = S < floor_rows ? floor_rows : S;
-    pl.S = S < kMinSplit ? kMinSplit : (S > kMaxSplit ? kMaxSplit : S);
-  }
-  pl.max_splits = s.max_ctx_len > 0 ? (s.max_ctx_len + pl.S - 1) / pl.S : 1;
-  pl.G = 0;
-  pl.nts = (s.W + 31) / 32;
-  pl.nseg = s.Hkv * pl.nRB;
-  pl.rows_block = 16 * pl.NR * pl.RB;
-  size_t rows = (size_t)s.B * pl.max_splits * s.Hkv * pl.R;
-  if (pl.kernel == kMfmaLds && s.B >= kStreamMinB && s.B <= kStreamMaxB) {
-    // stage count bound from max_ctx_len; the device splits the true count
-    const long seg_stages = (long)(s.max_ctx_len + 31) / 32 + pl.nts;
-    const long upper = (long)s.B * pl.nseg * seg_stages;
-    if (upper < (1L << 30)) {
-      pl.kernel = kMfmaStream;
-      const long slots = (long)kCUs * (pl.RB == 1 ? 2 : 1);
-      long per = s.split_tokens > 0 ? s.split_tokens / 32 : kMinStreamStages;
-      long G = (upper + per - 1) / per;
-      if (s.split_tokens == 0 && G > slots) G = slots;
-      pl.G = (int)(G < 1 ? 1 : (G > 65535 ? 65535 : G));
-      rows = ((size_t)pl.G + (size_t)s.B * pl.nseg) * pl.rows_block;
-    }
-  }
-  pl.acc_bytes = rows * s.D * sizeof(float);
-  pl.ml_offset = (pl.acc_bytes + 255) & ~(size_t)255;
-  pl.ml_bytes = rows * 2 * sizeof(float);
-  pl.seg_offset = (pl.ml_offset + pl.ml_bytes + 255) & ~(size_t)255;
-  pl.seg_bytes = pl.kernel == kMfmaStream ? (size_t)s.B * pl.nseg * 2 * sizeof(int) : 0;
-  return pl;
-}
 
 mtp_status launch_status() {
   return hipGetLastError() == hipSuccess ? MTP_OK : MTP_ERR_HIP;
