@@ -345,8 +345,13 @@ def bench_tree(wl: I.Workload, args) -> int:
     K, n_mask = 8, min(4, wl.W - 1)
     tin = I.make_tree_inputs(wl.B, K, wl.vocab, I.workload_seed(wl.name), device="cuda")
 
+    B, W = wl.B, wl.W
+    out = tuple(torch.empty(sz, dtype=torch.int32, device="cuda")
+                for sz in ((B, W), (B, W), (B, W), (B,)))
+    ws = torch.empty(B * K * W * 8 + 1024, dtype=torch.uint8, device="cuda")
+
     def launch():
-        lib.build_tree(tin["probs"], tin["root"], wl.W, n_mask)
+        lib.build_tree(tin["probs"], tin["root"], wl.W, n_mask, workspace=ws, out=out)
 
     ms = timed_graph(launch, args.steps, args.warmup)
     nbytes = wl.B * (K * wl.vocab * 4 + 4 + wl.W * 12 + 4)

@@ -354,12 +354,19 @@ mtp_status mtp_verify_attn_nested_combine(const mtp_shape* shape, const void* q,
  * parent -1), then the chosen nodes in the order chosen, then mask-token rows
  * (draft -1) chained from the deepest chosen top-1 node.  parents is a valid
  * TREE mask description and depth the position offset of each row;
- * n_nodes = 1 + chosen nodes.  Cost grows with V (each list is built by a
- * wave; V <= 1024 is held in registers). */
+ * n_nodes = 1 + chosen nodes.  V <= 4096.  Two launches: the ranked lists
+ * (a workgroup per depth and sequence), then the placement (a workgroup per
+ * sequence); `workspace` carries the lists between them. */
 mtp_status mtp_build_tree(int32_t B, int32_t K, int32_t V, int32_t W, int32_t n_mask,
                           const float* probs, const int32_t* root_token, float min_cum_prob,
                           int32_t* draft_ids, int32_t* parents, int32_t* depth,
-                          int32_t* n_nodes, void* stream);
+                          int32_t* n_nodes, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace of mtp_build_tree (the ranked candidate lists, caller-owned,
+ * 16-byte aligned; contents need no initialisation). */
+mtp_status mtp_build_tree_workspace_size(int32_t B, int32_t K, int32_t V, int32_t W,
+                                         int32_t n_mask, size_t* bytes);
 
 /* Positions of the block rows for the verifier's inputs, prepared on the
  * device ("BitMTP" Sec. 3.4 M3: verifier inputs follow the materialized KV

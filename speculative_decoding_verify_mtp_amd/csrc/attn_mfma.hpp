@@ -195,6 +195,8 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
   const int b = blockIdx.y;
   const Item it = decode_item(blockIdx.x * 4 + (threadIdx.x >> 6), p);
   if (it.split >= p.max_splits) return;
+  const int mkind = p.mask_kind[b];  // loaded with the context length
+  const int mid = lane_mask_id(p, b, lane);
   const int L = p.ctx_lens[b];
   if (L < 0 || L > p.max_ctx) return;  // reported by the combine
   const int ns = num_splits(L, p.S);
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
   if (last) {
     bool ok;
     const uint64_t vnode =
-        node_visibility(p.mask_kind[b], lane_mask_id(p, b, lane), p.W, p.lookback, lane, ok);
+        node_visibility(mkind, mid, p.W, p.lookback, lane, ok);
     if (ok) {
       uint64_t vrow[RB];
 #pragma unroll

@@ -191,6 +191,11 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
     nqs[k] = -kNestByteOffset * part;
   }
 
+  // the mask description goes out with the set-up loads: the last split
+  // needs it, and waiting for it after the context length would add a round
+  // trip before the first stage is issued
+  const int mkind = p.mask_kind[b];
+  const int mid = lane_mask_id(p, b, lane);
   const int L = p.ctx_lens[b];
   if (L < 0 || L > p.max_ctx) return;
   const int ns = num_splits(L, p.S);
@@ -392,7 +397,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
   if (last) {
     bool ok;
     const uint64_t vnode =
-        node_visibility(p.mask_kind[b], lane_mask_id(p, b, lane), p.W, p.lookback, lane, ok);
+        node_visibility(mkind, mid, p.W, p.lookback, lane, ok);
     if (ok) {
       uint64_t vrow[RB];
 #pragma unroll

@@ -507,15 +507,39 @@ mtp_status mtp_kv_commit_nested(const mtp_shape* shape, const void* k_new, const
   return launch_status();
 }
 
+static mtp_status check_tree(int32_t B, int32_t K, int32_t V, int32_t W, int32_t n_mask) {
+  if (B < 0 || B > 65535 || K < 1 || K > kTreeMaxK || V < 1 || V > kTreeMaxV || W < 1 ||
+      W > MTP_MAX_W || n_mask < 0 || n_mask > W - 1)
+    return MTP_ERR_SHAPE;
+  return MTP_OK;
+}
+
+static size_t tree_list_bytes(int32_t B, int32_t K, int32_t W, int32_t n_mask) {
+  return (size_t)B * K * (size_t)(W - n_mask) * 4;  // one int32 or fp32 array
+}
+
+mtp_status mtp_build_tree_workspace_size(int32_t B, int32_t K, int32_t V, int32_t W,
+                                         int32_t n_mask, size_t* bytes) {
+  const mtp_status st = check_tree(B, K, V, W, n_mask);
+  if (st != MTP_OK) return st;
+  if (bytes == nullptr) return MTP_ERR_NULL;
+  *bytes = 2 * ((tree_list_bytes(B, K, W, n_mask) + 255) & ~(size_t)255);
+  return MTP_OK;
+}
+
 mtp_status mtp_build_tree(int32_t B, int32_t K, int32_t V, int32_t W, int32_t n_mask,
                           const float* probs, const int32_t* root_token, float min_cum_prob,
                           int32_t* draft_ids, int32_t* parents, int32_t* depth,
-                          int32_t* n_nodes, void* stream) {
-  if (B < 0 || B > 65535 || K < 1 || K > kTreeMaxK || V < 1 || W < 1 || W > MTP_MAX_W ||
-      n_mask < 0 || n_mask > W - 1 || min_cum_prob != min_cum_prob)
-    return MTP_ERR_SHAPE;
+                          int32_t* n_nodes, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  mtp_status st = check_tree(B, K, V, W, n_mask);
+  if (st != MTP_OK) return st;
+  if (min_cum_prob != min_cum_prob) return MTP_ERR_SHAPE;
   if (B == 0) return MTP_OK;
-  if (!probs || !root_token || !draft_ids || !parents || !depth || !n_nodes) return MTP_ERR_NULL;
+  if (!probs || !root_token || !draft_ids || !parents || !depth || !n_nodes || !workspace)
+    return MTP_ERR_NULL;
+  const size_t half = (tree_list_bytes(B, K, W, n_mask) + 255) & ~(size_t)255;
+  if (workspace_bytes < 2 * half || ((uintptr_t)workspace & 15) != 0) return MTP_ERR_WORKSPACE;
   TreeParams p;
   p.probs = probs;
   p.root = root_token;
@@ -523,14 +547,18 @@ mtp_status mtp_build_tree(int32_t B, int32_t K, int32_t V, int32_t W, int32_t n_
   p.parent = parents;
   p.depth = depth;
   p.n_nodes = n_nodes;
+  p.list_tok = static_cast<int*>(workspace);
+  p.list_prb = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
   p.min_cum_prob = min_cum_prob;
   p.B = B;
   p.K = K;
   p.V = V;
   p.W = W;
   p.n_mask = n_mask;
-  const int threads = kWave * std::min(16, K);
-  tree_build_kernel<<<dim3(B), dim3(threads), 0, static_cast<hipStream_t>(stream)>>>(p);
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (W - 1 - n_mask > 0)
+    tree_lists_kernel<<<dim3(K, B), dim3(kTreeListThreads), 0, strm>>>(p);
+  tree_build_kernel<<<dim3(B), dim3(256), 0, strm>>>(p);
   return launch_status();
 }
 

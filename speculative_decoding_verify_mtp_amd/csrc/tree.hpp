@@ -2,14 +2,14 @@
 // Multi-Token Prediction via Embedding-Space Probing", Sec. 2.C and 2.D).
 // One workgroup per sequence.
 //
-// 1. Ranked lists: the waves take the probed depths in turn; for depth d a
-//    wave extracts the first n = slots + 1 tokens of p_d in the order
-//    (probability descending, id ascending) into LDS.  One token of a list
-//    may be the parent's and is skipped later, so slots + 1 entries always
-//    suffice.  Each round takes every lane's best entry ranked below the
-//    previous pick, then the wave's best of those; with V <= 1024 the lane's
-//    16 entries (ids lane + 64 j) stay in registers, larger vocabularies
-//    rescan the row.
+// 1. Ranked lists (tree_lists_kernel, one workgroup per depth and
+//    sequence): the first n = slots + 1 tokens of p_d in the order
+//    (probability descending, id ascending).  One token of a list may be the
+//    parent's and is skipped later, so slots + 1 entries always suffice.
+//    A radix selection of the n-th largest (probability, -id) key, then the
+//    n keys above it ordered by counting (see tree_lists_kernel; V <= 4096).
+//    The lists go through a workspace to tree_build_kernel (one workgroup
+//    per sequence), which does 2-4.
 // 2. Spine: wave 0 walks the depths in order: the top-1 token of depth d is
 //    the first list entry that differs from the spine token above, and
 //    c_d = c_{d-1} * p_d(spine) (fp32, in this order).
@@ -30,8 +30,6 @@ namespace mtpv {
 
 constexpr int kTreeMaxK = 64;
 constexpr int kTreeMaxList = MTP_MAX_W;  // slots + 1 <= W <= 64
-constexpr int kTreeRegElems = 16;        // entries per lane on the register path
-constexpr int kTreeRegV = kWave * kTreeRegElems;
 
 struct TreeParams {
   const float* probs;      // [B, K, V]
@@ -40,85 +38,105 @@ struct TreeParams {
   int32_t* parent;         // [B, W]
   int32_t* depth;          // [B, W]
   int32_t* n_nodes;        // [B]
+  int* list_tok;           // workspace [B, K, n]
+  float* list_prb;         // workspace [B, K, n]
   float min_cum_prob;
   int B, K, V, W, n_mask;
 };
 
-// (p, i) ranks above (q, j): more probable, or as probable with a smaller id.
-// Bitwise operators: no short-circuit branches in the unrolled scans.
-__device__ __forceinline__ bool rank_above(float p, int i, float q, int j) {
-  return (p > q) | ((p == q) & (i < j));
-}
+constexpr int kTreeListThreads = 256;
+constexpr int kTreeListElems = 16;  // entries per thread: V <= 4096
+constexpr int kTreeMaxV = kTreeListThreads * kTreeListElems;
 
-// Wave argmax of (p, i) by rank (every lane gets the winner).
-__device__ __forceinline__ void wave_best(float& p, int& i) {
+// Ranked list of one (sequence, depth) by radix selection, one workgroup
+// per (depth, sequence).  Entry (p, i) gets the 64-bit key
+// (bits of p) << 32 | ~i: p >= 0, so a larger key ranks higher (more
+// probable, then smaller id) and every key is distinct and non-zero.  Eight
+// passes over 8-bit digits, most significant first, find the k-th largest
+// key (k = min(n, V)): each pass histograms the digit of the keys that match
+// the digits found so far (LDS atomics) and wave 0 walks the bins from the
+// top.  The k keys at or above it are then appended to LDS and put in order
+// by counting, for each, the keys above it.
+__global__ __launch_bounds__(kTreeListThreads) void tree_lists_kernel(TreeParams p) {
+  __shared__ int s_hist[256];
+  __shared__ unsigned long long s_prefix;
+  __shared__ int s_k, s_cnt;
+  __shared__ unsigned long long s_key[kTreeMaxList];
+  const int d = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int n = p.W - p.n_mask;  // slots + 1
+  const float* row = p.probs + ((size_t)b * p.K + d) * p.V;
+  unsigned long long key[kTreeListElems];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float q = __shfl_xor(p, o);
-    const int j = __shfl_xor(i, o);
-    const bool take = rank_above(q, j, p, i);
-    p = take ? q : p;
-    i = take ? j : i;
+  for (int j = 0; j < kTreeListElems; ++j) {
+    const int i = tid + kTreeListThreads * j;
+    const float x = row[min(i, p.V - 1)];
+    key[j] = i < p.V ? ((unsigned long long)__float_as_uint(x) << 32) | (unsigned)(~i) : 0ull;
   }
-}
-
-// The first n entries of one probability row by rank into (tok, prb);
-// entries past the vocabulary get token -1, probability -1.
-template <bool kRegs>
-__device__ __forceinline__ void ranked_list(const float* row, int V, int n, int* tok, float* prb) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (kRegs) {
-    float p[kTreeRegElems];
+  const int kk = min(n, p.V);
+  unsigned long long prefix = 0ull;
+  int k = kk;
+  for (int pass = 7; pass >= 0; --pass) {
+    s_hist[tid] = 0;
+    __syncthreads();
+    const int sh = 8 * pass;
+    const unsigned long long hmask = pass == 7 ? 0ull : (~0ull << (sh + 8));
 #pragma unroll
-    for (int j = 0; j < kTreeRegElems; ++j) {
-      const int i = lane + kWave * j;
-      p[j] = row[min(i, V - 1)];  // unconditional (in-bounds) load, then select
-      p[j] = i < V ? p[j] : -1.f;
-    }
-    // each round: every lane's best entry below the previous pick, then the
-    // wave's best of those
-    float pp = __builtin_inff();
-    int pi = -1;
-    for (int r = 0; r < n; ++r) {
-      float bp = -1.f;
-      int bi = 0x7fffffff;
+    for (int j = 0; j < kTreeListElems; ++j)
+      if (key[j] != 0ull && (key[j] & hmask) == (prefix & hmask))
+        atomicAdd(&s_hist[(int)((key[j] >> sh) & 255ull)], 1);
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l takes bins 255 - 4l, ..., 252 - 4l (from the top)
+      int c[4], sum = 0;
 #pragma unroll
-      for (int j = 0; j < kTreeRegElems; ++j) {
-        const int i = lane + kWave * j;
-        const bool take = (p[j] >= 0.f) & rank_above(pp, pi, p[j], i) & rank_above(p[j], i, bp, bi);
-        bp = take ? p[j] : bp;
-        bi = take ? i : bi;
+      for (int u = 0; u < 4; ++u) {
+        c[u] = s_hist[255 - 4 * lane - u];
+        sum += c[u];
       }
-      wave_best(bp, bi);
-      if (lane == 0) {
-        tok[r] = bp >= 0.f ? bi : -1;
-        prb[r] = bp >= 0.f ? bp : -1.f;
+      int incl = sum;  // inclusive scan over lanes
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
       }
-      pp = bp;
-      pi = bi;
-    }
-  } else {
-    float pp = __builtin_inff();
-    int pi = -1;
-    for (int r = 0; r < n; ++r) {
-      float bp = -1.f;
-      int bi = 0x7fffffff;
-      for (int i = lane; i < V; i += kWave) {
-        const float x = row[i];
-        const bool below = rank_above(pp, pi, x, i);
-        if (below && rank_above(x, i, bp, bi)) {
-          bp = x;
-          bi = i;
+      const int before = incl - sum;
+      if (before < k && k <= incl) {
+        int acc = before;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (acc < k && k <= acc + c[u]) {
+            s_prefix = prefix | ((unsigned long long)(255 - 4 * lane - u) << sh);
+            s_k = k - acc;
+          }
+          acc += c[u];
         }
       }
-      wave_best(bp, bi);
-      if (lane == 0) {
-        tok[r] = bp >= 0.f ? bi : -1;
-        prb[r] = bp >= 0.f ? bp : -1.f;
-      }
-      pp = bp;
-      pi = bi;
     }
+    __syncthreads();
+    prefix = s_prefix;
+    k = s_k;
+  }
+  // the kk keys at or above the kk-th largest
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kTreeListElems; ++j)
+    if (key[j] != 0ull && key[j] >= prefix) s_key[atomicAdd(&s_cnt, 1)] = key[j];
+  __syncthreads();
+  int* out_tok = p.list_tok + ((size_t)b * p.K + d) * n;
+  float* out_prb = p.list_prb + ((size_t)b * p.K + d) * n;
+  if (tid < kk) {
+    const unsigned long long mine = s_key[tid];
+    int r = 0;
+    for (int t = 0; t < kk; ++t) r += s_key[t] > mine ? 1 : 0;
+    out_tok[r] = (int)(~(unsigned)(mine & 0xffffffffull));
+    out_prb[r] = __uint_as_float((unsigned)(mine >> 32));
+  } else if (tid < n) {
+    out_tok[tid] = -1;
+    out_prb[tid] = -1.f;
   }
 }
 
@@ -159,22 +177,18 @@ __global__ __launch_bounds__(1024) void tree_build_kernel(TreeParams p) {
   __shared__ int s_nsel, s_deep;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
   const int W = p.W;
   const int slots = W - 1 - p.n_mask;
   const int n = slots + 1;
   const int K = p.K;
   const int root = p.root[b];
 
-  // 1. ranked lists
+  // 1. ranked lists (tree_lists_kernel) into LDS
   if (slots > 0) {
-    for (int d = wv; d < K; d += nw) {
-      const float* row = p.probs + ((size_t)b * K + d) * p.V;
-      if (p.V <= kTreeRegV)
-        ranked_list<true>(row, p.V, n, s_tok[d], s_prb[d]);
-      else
-        ranked_list<false>(row, p.V, n, s_tok[d], s_prb[d]);
+    for (int e = threadIdx.x; e < K * n; e += blockDim.x) {
+      const int d = e / n, r = e - d * n;
+      s_tok[d][r] = p.list_tok[((size_t)b * K + d) * n + r];
+      s_prb[d][r] = p.list_prb[((size_t)b * K + d) * n + r];
     }
   }
   if (threadIdx.x < kTreeMaxK) s_spine_row[threadIdx.x] = -1;

@@ -27,7 +27,8 @@ EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_si
            "mtp_verify_step", "mtp_kv_quantize", "mtp_kv_commit_nested",
            "mtp_verify_attn_nested_workspace_size", "mtp_verify_attn_nested",
            "mtp_verify_attn_nested_partial", "mtp_verify_attn_nested_combine",
-           "mtp_build_tree", "mtp_block_positions", "mtp_get_device_status")
+           "mtp_build_tree", "mtp_build_tree_workspace_size", "mtp_block_positions",
+           "mtp_get_device_status")
 _ATTN_FN = {"both": "mtp_verify_attn", "partial": "mtp_verify_attn_partial",
             "combine": "mtp_verify_attn_combine"}
 _NESTED_FN = {"both": "mtp_verify_attn_nested", "partial": "mtp_verify_attn_nested_partial",
@@ -100,7 +101,9 @@ def load() -> ctypes.CDLL:
         getattr(lib, fn).restype = _i32
         getattr(lib, fn).argtypes = [sp, _vp, npp] + [_vp] * 6 + [_i32, _vp, _vp, _vp, _sz, _vp]
     lib.mtp_build_tree.restype = _i32
-    lib.mtp_build_tree.argtypes = [_i32] * 5 + [_vp, _vp, ctypes.c_float] + [_vp] * 4 + [_vp]
+    lib.mtp_build_tree.argtypes = [_i32] * 5 + [_vp, _vp, ctypes.c_float] + [_vp] * 5 + [_sz, _vp]
+    lib.mtp_build_tree_workspace_size.restype = _i32
+    lib.mtp_build_tree_workspace_size.argtypes = [_i32] * 5 + [ctypes.POINTER(_sz)]
     lib.mtp_block_positions.restype = _i32
     lib.mtp_block_positions.argtypes = [sp] + [_vp] * 4 + [_vp]
     lib.mtp_get_device_status.restype = _i32
@@ -454,18 +457,27 @@ def verify_attn_nested(q, kv: NestedKV, block_table, ctx_lens, k_new, v_new, mas
     return out, lse
 
 
-def build_tree(probs, root_token, W, n_mask, min_cum_prob=0.0, *, stream=None):
+def build_tree(probs, root_token, W, n_mask, min_cum_prob=0.0, *, workspace=None, out=None,
+               stream=None):
     """Dynamic token tree; returns (draft_ids, parents, depth [B, W], n_nodes [B]) int32."""
     lib = load()
     B, K, V = probs.shape
     dev = probs.device
-    draft = torch.empty((B, W), dtype=torch.int32, device=dev)
-    parents = torch.empty((B, W), dtype=torch.int32, device=dev)
-    depth = torch.empty((B, W), dtype=torch.int32, device=dev)
-    n_nodes = torch.empty(B, dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty((B, W), dtype=torch.int32, device=dev),
+               torch.empty((B, W), dtype=torch.int32, device=dev),
+               torch.empty((B, W), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    draft, parents, depth, n_nodes = out
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check("mtp_build_tree_workspace_size",
+               lib.mtp_build_tree_workspace_size(B, K, V, W, n_mask, ctypes.byref(n)))
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
     _check("mtp_build_tree", lib.mtp_build_tree(
         B, K, V, W, n_mask, _ptr(probs), _ptr(root_token), float(min_cum_prob), _ptr(draft),
-        _ptr(parents), _ptr(depth), _ptr(n_nodes), _stream(stream)))
+        _ptr(parents), _ptr(depth), _ptr(n_nodes), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
     return draft, parents, depth, n_nodes
 
 

@@ -19,7 +19,7 @@ CASES = [  # B, K, V, W, n_mask, min_cum_prob, peak
     (2, 16, 50, 20, 3, 0.0, 2.0),
     (2, 1, 30, 10, 2, 0.0, 8.0),
     (5, 20, 7, 40, 5, 0.0, 1.0),
-    (2, 3, 5000, 24, 2, 0.0, 8.0),   # rescanning path (V > 1024)
+    (2, 3, 4096, 24, 2, 0.0, 8.0),   # the largest vocabulary
     (2, 64, 200, 64, 8, 0.0, 8.0),
     (3, 6, 100, 1, 0, 0.0, 8.0),     # W = 1: the root only
     (3, 6, 100, 8, 7, 0.0, 8.0),     # no predicted rows
@@ -83,3 +83,9 @@ def test_block_positions_match_oracle(masks):
     h = inp["host"]
     assert np.array_equal(ints(got), O.block_positions(h["ctx_lens"], h["mask_kind"],
                                                         h["mask_ids"]))
+
+
+def test_tree_rejects_vocabularies_above_4096():
+    inp = I.make_tree_inputs(1, 2, 4097, 5, device="cuda")
+    with pytest.raises(lib.MtpError):
+        lib.build_tree(inp["probs"], inp["root"], 8, 1)
