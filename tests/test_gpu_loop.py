@@ -108,3 +108,42 @@ def test_graph_captured_decode_loop(masks):
         assert np.array_equal(gctx, rctx)
         assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
     assert (rctx - host["ctx_lens"] >= N).all()
+
+
+def test_tree_builder_feeds_the_step_on_the_device():
+    """Drafter probabilities -> dynamic tree (block of the next step) ->
+    positions -> verify step (tree mask from the builder) -> commit, all on
+    the device; the oracle takes the same path on the CPU."""
+    B, W, n_mask, K = 3, 16, 3, 6
+    wl = I.Workload(name="tree_step", B=B, Hq=8, Hkv=2, D=128, W=W, dtype="bf16", ctx_lo=40,
+                    ctx_hi=300, masks="tree")
+    banner(f"tree -> step {wl}")
+    base = I.make_inputs(wl, 61, device="cuda")
+    tin = I.make_tree_inputs(B, K, wl.vocab, 62, device="cuda")
+    root = base["draft_ids"][:, 0].contiguous()  # any token: the anchor
+    draft, parents, depth, n_nodes = lib.build_tree(tin["probs"], root, W, n_mask)
+    kinds = torch.full((B,), lib.MASK_TREE, dtype=torch.uint8, device="cuda")
+    pos = lib.block_positions(base["ctx_lens"], kinds, parents)
+    kc, vc = base["k_cache"].clone(), base["v_cache"].clone()
+    out, lse, alen, apath, bonus, ctx_out = lib.verify_step(
+        base["q"], kc, vc, base["block_table"], base["ctx_lens"], base["k_new"], base["v_new"],
+        kinds, parents, base["logits"], draft, scale=base["scale"])
+    torch.cuda.synchronize()
+    assert lib.device_status(clear=True) == 0
+    h = base["host"]
+    rd, rp, rdep, rn = O.dynamic_tree(tin["host"]["probs"], ints(root), W, n_mask)
+    assert np.array_equal(ints(draft), rd) and np.array_equal(ints(parents), rp)
+    assert np.array_equal(ints(pos), O.block_positions(h["ctx_lens"], ints(kinds), rp))
+    assert np.array_equal(ints(pos), h["ctx_lens"][:, None] + rdep)
+    ref_out, ref_lse = O.verify_attention(f64(base["q"]), f64(base["k_cache"]),
+                                          f64(base["v_cache"]), h["block_table"], h["ctx_lens"],
+                                          f64(base["k_new"]), f64(base["v_new"]), ints(kinds), rp,
+                                          base["scale"])
+    assert_attn_close(out, lse, ref_out, ref_lse, ATOL, RTOL, "tree step")
+    ra = O.accept(base["logits"].cpu().numpy(), rd, ints(kinds), rp)
+    assert np.array_equal(ints(alen), ra[0]) and np.array_equal(ints(apath), ra[1])
+    assert np.array_equal(ints(bonus), ra[2])
+    rk, rv, rctx = O.kv_commit(raw(base["k_cache"]), raw(base["v_cache"]), raw(base["k_new"]),
+                               raw(base["v_new"]), ra[0], ra[1], h["block_table"], h["ctx_lens"])
+    assert np.array_equal(ints(ctx_out), rctx)
+    assert np.array_equal(raw(kc), rk) and np.array_equal(raw(vc), rv)
