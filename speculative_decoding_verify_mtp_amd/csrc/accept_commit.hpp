@@ -47,7 +47,8 @@ struct CommitParams {
 
 // Inputs of wave 0 loaded before the argmax, so that their latency overlaps
 // the logits stream: this lane's mask id and draft id, the mask kind, and for
-// the commit the context length and the page of slot ctx + lane.
+// the commit the context length; the page of slot ctx + lane follows once the
+// context length is back (commit_page).
 struct Prefetch {
   int kind, id, draft, L, page;
 };
@@ -59,15 +60,17 @@ __device__ __forceinline__ Prefetch prefetch_inputs(const AcceptParams& ap, cons
   f.kind = ap.mask_kind[b];
   f.id = lane < W ? ap.mask_ids[(size_t)b * W + lane] : 0;
   f.draft = lane < W ? ap.draft_ids[(size_t)b * W + lane] : -1;
-  f.L = 0;
+  f.L = cp != nullptr ? cp->ctx_in[b] : 0;
   f.page = -1;
-  if (cp != nullptr) {
-    f.L = cp->ctx_in[b];
-    const int t = f.L + lane;
-    const int pi = t >> 4;
-    if (lane < W && f.L >= 0 && pi < cp->max_pages) f.page = cp->block_table[(size_t)b * cp->max_pages + pi];
-  }
   return f;
+}
+
+// Page of the commit slot ctx + lane (-1 past the block, the table or for a
+// negative context length).
+__device__ __forceinline__ int commit_page(const CommitParams& cp, int b, int L) {
+  const int lane = threadIdx.x & 63;
+  const int pi = (L + lane) >> 4;
+  return (lane < cp.W && L >= 0 && pi < cp.max_pages) ? cp.block_table[(size_t)b * cp.max_pages + pi] : -1;
 }
 
 // Argmax of one logits row by one wave (smallest id on ties); 16-byte
@@ -174,20 +177,28 @@ __device__ __forceinline__ int reg_row_argmax(const RegRow& r, int V) {
 }
 
 // Argmax of every block row into s_tgt[0..W).  All waves take part, row i
-// on wave i % waves.
-__device__ __forceinline__ void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
+// on wave i % waves.  `mid()` runs once per thread, right after the loads of
+// the thread's first register pass are issued (at the start otherwise): loads
+// it issues queue behind the logits, not in front of them.
+template <typename Mid>
+__device__ __forceinline__ void block_argmax(const AcceptParams& p, int b, int* s_tgt, Mid mid) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const bool vec = rows_vec(p.logits, p.V);
   const float* base = p.logits + (size_t)b * p.W * p.V;
   if (vec && p.V <= kRegV) {
+    bool mid_done = false;  // wave-uniform
     for (int i0 = wv; i0 < p.W; i0 += nw * kRegRows) {
       RegRow rr[kRegRows];
 #pragma unroll
       for (int r = 0; r < kRegRows; ++r) {
         const int i = i0 + r * nw;
         if (i < p.W) load_reg_row(base + (size_t)i * p.V, p.V, rr[r]);
+      }
+      if (!mid_done) {
+        mid();
+        mid_done = true;
       }
 #pragma unroll
       for (int r = 0; r < kRegRows; ++r) {
@@ -198,12 +209,18 @@ __device__ __forceinline__ void block_argmax(const AcceptParams& p, int b, int* 
         }
       }
     }
+    if (!mid_done) mid();
     return;
   }
+  mid();
   for (int i = wv; i < p.W; i += nw) {
     const int bi = wave_row_argmax(base + (size_t)i * p.V, p.V, vec);
     if (lane == 0) s_tgt[i] = bi;
   }
+}
+
+__device__ __forceinline__ void block_argmax(const AcceptParams& p, int b, int* s_tgt) {
+  block_argmax(p, b, s_tgt, [] {});
 }
 
 // Acceptance structure of block node `lane` (wave 0, lane = node): its
@@ -400,9 +417,11 @@ constexpr int kAcceptScratchInts = 4 * MTP_MAX_W + 2;
 
 // Acceptance then commit of sequence b by one workgroup (any number of
 // waves; wave 0 does the per-node work).  `sm` is kAcceptScratchInts ints of
-// LDS.  The block's new K/V rows are fetched into registers at the start,
-// beside the logits, when they fit (kPre 16-byte chunks per thread and
-// tensor); the commit is then only stores.
+// LDS.  Load order, heads of the dependency chains first: wave 0's per-node
+// inputs and the context length, then the logits rows, then the block's new
+// K/V rows (into registers when they fit, kPre 16-byte chunks per thread and
+// tensor: the commit is then only stores) and the commit pages, which need
+// the context length and are only used after the acceptance.
 __device__ __forceinline__ void accept_commit_seq(const AcceptParams& ap, const CommitParams& cp, int b,
                                          int* sm) {
   constexpr int kPre = 4;
@@ -419,21 +438,23 @@ __device__ __forceinline__ void accept_commit_seq(const AcceptParams& ap, const 
   const char* vn = static_cast<const char*>(cp.v_new);
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   u32x4 pk[kPre], pv[kPre];
-  if (pre) {
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      const int idx = threadIdx.x + u * blockDim.x;
-      if (idx < all) {
-        const int row = idx / chunks;
-        const size_t src = ((size_t)b * ap.W + row) * cp.row_bytes + (size_t)(idx - row * chunks) * 16;
-        pk[u] = *reinterpret_cast<const u32x4*>(kn + src);
-        pv[u] = *reinterpret_cast<const u32x4*>(vn + src);
-      }
-    }
-  }
   Prefetch f{};
   if (threadIdx.x < kWave) f = prefetch_inputs(ap, &cp, b);
-  block_argmax(ap, b, s_tgt);
+  block_argmax(ap, b, s_tgt, [&] {
+    if (pre) {
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        const int idx = threadIdx.x + u * blockDim.x;
+        if (idx < all) {
+          const int row = idx / chunks;
+          const size_t src = ((size_t)b * ap.W + row) * cp.row_bytes + (size_t)(idx - row * chunks) * 16;
+          pk[u] = *reinterpret_cast<const u32x4*>(kn + src);
+          pv[u] = *reinterpret_cast<const u32x4*>(vn + src);
+        }
+      }
+    }
+    if (threadIdx.x < kWave) f.page = commit_page(cp, b, f.L);
+  });
   __syncthreads();
   if (threadIdx.x < kWave) {
     const int a = wave_accept(ap, b, f, s_tgt, s_path);
