@@ -420,11 +420,12 @@ constexpr int kAcceptScratchInts = 4 * MTP_MAX_W + 2;
 // LDS.  Load order, heads of the dependency chains first: wave 0's per-node
 // inputs and the context length, then the logits rows, then the block's new
 // K/V rows (into registers when they fit, kPre 16-byte chunks per thread and
-// tensor: the commit is then only stores) and the commit pages, which need
-// the context length and are only used after the acceptance.
+// tensor, up to kPreMaxBytes: the commit is then only stores) and the commit
+// pages, which need the context length and are only used after the acceptance.
 __device__ __forceinline__ void accept_commit_seq(const AcceptParams& ap, const CommitParams& cp, int b,
                                          int* sm) {
   constexpr int kPre = 4;
+  constexpr int kPreMaxBytes = 32 * 1024;
   int* s_tgt = sm;
   int* s_path = sm + MTP_MAX_W;
   int* s_pos = sm + 2 * MTP_MAX_W;  // path position of a block row, -1 if not committed
@@ -433,7 +434,9 @@ __device__ __forceinline__ void accept_commit_seq(const AcceptParams& ap, const 
   const int lane = threadIdx.x & 63;
   const int chunks = cp.row_bytes >> 4;
   const int all = ap.W * chunks;
-  const bool pre = all <= kPre * (int)blockDim.x;
+  // one compute unit streams everything this workgroup loads: the rows of a
+  // large block are fetched after the acceptance instead, and only if accepted
+  const bool pre = all <= kPre * (int)blockDim.x && 2 * all * 16 <= kPreMaxBytes;
   const char* kn = static_cast<const char*>(cp.k_new);
   const char* vn = static_cast<const char*>(cp.v_new);
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
