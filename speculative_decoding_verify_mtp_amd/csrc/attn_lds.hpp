@@ -311,8 +311,7 @@ void attn_partial_lds(AttnParams p) {
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
     float l = st.l[k];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = rows4_sum(l);
     const int rho = (row_tile0 + k) * 16 + c;
     if (rho < p.R) {
       const size_t pidx =

@@ -134,8 +134,7 @@ __device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
       if (!vis(k, e)) x[e] = neg_inf();
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                      fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows4_max(mx);
     mx *= scale_log2;
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
@@ -336,8 +335,7 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
     float l = st.l[k];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = rows4_sum(l);
     const int rho = (it.rb * RB + k) * 16 + c;
     if (rho < p.R) {
       const size_t pidx =

@@ -106,8 +106,7 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                      fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows4_max(mx);
     mx *= sl2;
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
@@ -186,8 +185,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
 #pragma unroll
       for (int m = 0; m < NC; ++m) qf[k][m] = bf16x8{};
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
+    part = rows4_sum(part);
     nqs[k] = -kNestByteOffset * part;
   }
 
@@ -384,8 +382,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
     float lrow = lp[k];
-    lrow += __shfl_xor(lrow, 16);
-    lrow += __shfl_xor(lrow, 32);
+    lrow = rows4_sum(lrow);
     const float off = -kNestByteOffset * 0.0625f * lrow;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -445,8 +442,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
     float l = st.l[k];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = rows4_sum(l);
     const int rho = (row_tile0 + k) * 16 + c;
     if (rho < p.R) {
       const size_t pidx =

@@ -304,8 +304,7 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
 #pragma unroll
       for (int k = 0; k < RB; ++k) {
         float l = st.l[k];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        l = rows4_sum(l);
         const int rl = (wv * RB + k) * 16 + c;  // row within the block
         const int rho = rb * sp.rows_block + rl;
         if (rho < p.R) {

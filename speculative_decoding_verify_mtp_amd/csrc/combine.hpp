@@ -178,8 +178,7 @@ __device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamPa
   }
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
-    a[j] += __shfl_xor(a[j], 16);
-    a[j] += __shfl_xor(a[j], 32);
+    a[j] = rows4_sum(a[j]);
   }
   const float inv = 1.f / den;
   if (gq == 0) {
