@@ -63,6 +63,13 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
   const int start = it.split * p.S;
   const int end = min(L, start + p.S);
   const bool last = it.split == ns - 1;
+  // the split's page indices, lane i holding entries i and 64 + i (a split
+  // spans at most 128 pages)
+  const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
+  const int pbase = start >> 4;
+  const int pavail = p.max_pages - pbase;
+  const int pr0 = lane < pavail ? btrow[pbase + lane] : 0;
+  const int pr1 = lane + 64 < pavail ? btrow[pbase + lane + 64] : 0;
 
   const T* qbase = static_cast<const T*>(p.q);
   const T* kc = static_cast<const T*>(p.k_cache) + (size_t)it.kvh * D + sub * 16;
@@ -114,19 +121,24 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
     for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
   }
 
-  const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
   const int ncomm = end - start;
   const int n = ncomm + ntail;
   bool bad = false;
   for (int k0 = 0; k0 < n; k0 += KG) {
     const int kk = k0 + kg;
     const bool valid = kk < n;
+    // the page of key kk from the split's page list (pr0, pr1 above): one
+    // memory round trip per step instead of two.  The shuffle runs with the
+    // whole wave active (the list lanes are not those of the key).
+    const int pi = ((start + min(kk, max(ncomm - 1, 0))) >> 4) - pbase;
+    const int a0 = __shfl(pr0, pi & 63);
+    const int a1 = __shfl(pr1, pi & 63);
     const T* kp;
     const T* vp;
     int jb = -1;  // in-block key index, -1 for committed keys
     if (kk < ncomm) {
       const int t = start + kk;
-      int pg = btrow[t >> 4];
+      int pg = pi < 64 ? a0 : a1;
       if ((unsigned)pg >= (unsigned)p.num_pages) {
         bad = true;
         pg = 0;

@@ -72,6 +72,19 @@ def test_split_size_does_not_change_the_result(split):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"split {split}")
 
 
+@pytest.mark.parametrize("split", [64, 1024, 2048])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_valu_long_splits_match_oracle(split, dtype):
+    # fewer than 16 rows per KV head: the vector-ALU kernel, whose splits
+    # span up to 128 pages and end on ragged steps of the key groups
+    wl = W_("valu_long", B=3, Hq=4, Hkv=2, W=3, dtype=dtype, ctx_lo=1500, ctx_hi=2600,
+            masks="mixed")
+    inp = gpu_inputs(wl, 11)
+    out, lse = run_attn(inp, split_tokens=split)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"valu split {split} {dtype}")
+
+
 def test_batch_above_the_stream_table_uses_per_split_items():
     """More than 1024 sequences: the per-split LDS kernel instead of the
     stream schedule (its stage table holds 1024 sequences)."""
