@@ -25,8 +25,9 @@
 //     {4q..4q+3} of tile 0 and of tile 1 -- exactly the S^T registers.
 //   * acc^T accumulator: lane (j, q) ends up owning row j, d in
 //     [q * D/4, (q+1) * D/4).
-// K and V go straight from HBM to registers with 16-byte (D=128) or 8-byte
-// (D=64) loads; no LDS is needed.  Online softmax runs in the log2 domain.
+// In attn_partial_mfma (launched for D = 64; D = 128 runs the same tile
+// step from the LDS ring kernels) K and V go straight from HBM to registers
+// with 8-byte loads; no LDS is needed.  Online softmax runs in the log2 domain.
 #pragma once
 
 #include "common.hpp"
@@ -236,13 +237,26 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
     for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Committed keys [start, end), 32 per step (two pages; start is a multiple of 32).
+  // Committed keys [start, end), 32 per step (two pages; start is a multiple
+  // of 32).  The split's page indices are held in two registers per lane
+  // (lane i: entries i and 64 + i; a split spans at most 128 pages), and the
+  // K/V rows of the next step are requested before the current step is
+  // reduced: one memory round trip per step, overlapped with the compute.
   const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
+  const int pbase = start >> 4;
+  const int pavail = p.max_pages - pbase;
+  const int pr0 = lane < pavail ? btrow[pbase + lane] : 0;
+  const int pr1 = lane + 64 < pavail ? btrow[pbase + lane + 64] : 0;
   bool bad = false;
-  for (int t0 = start; t0 < end; t0 += 32) {
+  struct Step {
+    bf16x8 kf[2][NC];
+    VRow<D> vv[8];
+  };
+  auto load_step = [&](int t0, Step& d) __attribute__((always_inline)) {
     const int nk = end - t0;  // keys of this tile that are committed (may exceed 32)
-    int pg0 = btrow[t0 >> 4];
-    int pg1 = nk > 16 ? btrow[(t0 >> 4) + 1] : pg0;
+    const int pi = (t0 >> 4) - pbase;  // wave-uniform
+    int pg0 = __builtin_amdgcn_readlane(pi < 64 ? pr0 : pr1, pi & 63);
+    int pg1 = nk > 16 ? __builtin_amdgcn_readlane(pi + 1 < 64 ? pr0 : pr1, (pi + 1) & 63) : pg0;
     if ((unsigned)pg0 >= (unsigned)p.num_pages) {
       bad = true;
       pg0 = 0;
@@ -253,7 +267,6 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
     }
     // Keys past the committed range load the tile's first row (always valid)
     // and are masked out of the softmax.
-    bf16x8 kf[2][NC];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = kt * 16 + c;
@@ -262,22 +275,35 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
       const int slot = v ? c : 0;
       const uint16_t* src = kc + ((size_t)pg * kPage + slot) * slot_stride + qd * 8;
 #pragma unroll
-      for (int m = 0; m < NC; ++m) kf[kt][m] = load_bf16x8(src + m * 32);
+      for (int m = 0; m < NC; ++m) d.kf[kt][m] = load_bf16x8(src + m * 32);
     }
-    VRow<D> vv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int key = pv_key(qd, e);
       const bool v = key < nk;
       const int pg = v ? (e < 4 ? pg0 : pg1) : pg0;
       const int slot = v ? (key & 15) : 0;
-      vv[e] = load_vrow<D>(vc + ((size_t)pg * kPage + slot) * slot_stride + c * VE);
+      d.vv[e] = load_vrow<D>(vc + ((size_t)pg * kPage + slot) * slot_stride + c * VE);
     }
+  };
+  auto step = [&](int t0, const Step& d) __attribute__((always_inline)) {
+    const int nk = end - t0;
     if (nk >= 32) {
-      mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [](int, int) { return true; });
+      mfma_tile<D, RB>(qf, d.kf, d.vv, p.scale_log2, st, [](int, int) { return true; });
     } else {
-      mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st,
+      mfma_tile<D, RB>(qf, d.kf, d.vv, p.scale_log2, st,
                        [&](int, int e) { return (e < 4 ? 4 * qd + e : 16 + 4 * qd + e - 4) < nk; });
+    }
+  };
+  if (start < end) {
+    Step s0, s1;  // ping-pong: s0 holds steps t0, s1 steps t0 + 32
+    load_step(start, s0);
+    for (int t0 = start; t0 < end; t0 += 64) {
+      if (t0 + 32 < end) load_step(t0 + 32, s1);
+      step(t0, s0);
+      if (t0 + 32 >= end) break;
+      if (t0 + 64 < end) load_step(t0 + 64, s0);
+      step(t0 + 32, s1);
     }
   }
 

@@ -160,16 +160,10 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
     else attn_partial_lds<1, 1><<<wgrid, wblock, 0, strm>>>(p);
   } else {
     const dim3 grid((unsigned)((items + 3) / 4), (unsigned)B);
-    if (pl.kernel == kMfmaDirect) {
-      if (D == 128) {
-        if (pl.RB == 4) attn_partial_mfma<128, 4><<<grid, block, 0, strm>>>(p);
-        else if (pl.RB == 2) attn_partial_mfma<128, 2><<<grid, block, 0, strm>>>(p);
-        else attn_partial_mfma<128, 1><<<grid, block, 0, strm>>>(p);
-      } else {
-        if (pl.RB == 4) attn_partial_mfma<64, 4><<<grid, block, 0, strm>>>(p);
-        else if (pl.RB == 2) attn_partial_mfma<64, 2><<<grid, block, 0, strm>>>(p);
-        else attn_partial_mfma<64, 1><<<grid, block, 0, strm>>>(p);
-      }
+    if (pl.kernel == kMfmaDirect) {  // D = 64 only (D = 128 takes the LDS kernels)
+      if (pl.RB == 4) attn_partial_mfma<64, 4><<<grid, block, 0, strm>>>(p);
+      else if (pl.RB == 2) attn_partial_mfma<64, 2><<<grid, block, 0, strm>>>(p);
+      else attn_partial_mfma<64, 1><<<grid, block, 0, strm>>>(p);
     } else if (dtype == MTP_F32) {
       if (D == 128) attn_partial_valu<float, 128><<<grid, block, 0, strm>>>(p);
       else attn_partial_valu<float, 64><<<grid, block, 0, strm>>>(p);
