@@ -96,18 +96,35 @@ __device__ __forceinline__ void wait_stage_barrier(int n) {
     wait_vmem_barrier<3 * PER>();
 }
 
+// Merge of a key slice's softmax state into slice 0's, lane by lane (the
+// slices hold the same rows in the same lanes).  Stored per lane as 32
+// accumulators, the reference max and the lane's share of the row sum.
+constexpr int kSliceStateFloats = 34;
+
 // RB = 1 kernels are held to 256 registers so that two waves share a SIMD.
-template <int RB, int NR>
-__global__ __launch_bounds__(64 * NR) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
+// KS > 1 (key slices): the workgroup has NR * KS waves; wave (g, k) owns the
+// row tiles of group g and the stages k, k + KS, ... of the item, and the KS
+// softmax states of a row tile are merged through LDS at the end.  A split
+// whose stages all fit the ring is then one wait and one barrier, and each
+// wave reduces 1 / KS of its stages: for short splits (a single sequence,
+// latency-bound) the per-stage compute chain is the critical path.
+template <int RB, int NR, int KS = 1>
+__global__ __launch_bounds__(64 * NR * KS) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
 void attn_partial_lds(AttnParams p) {
   constexpr int D = 128;
   constexpr int NC = D / 32;
   constexpr int NT = D / 16;
-  constexpr int IPW = 16 / NR;  // images per wave per stage
+  constexpr int NW = NR * KS;   // waves
+  constexpr int IPW = 16 / NW;  // images per wave per stage
+  static_assert(KS == 1 || RB == 1, "key slices are used with one row tile per wave");
+  static_assert(KS == 1 || NW * RB * kSliceStateFloats * 4 * kWave <= kLdsStages * kStageBytes,
+                "slice states must fit the ring");
   __shared__ __attribute__((aligned(16))) char ring[kLdsStages * kStageBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = threadIdx.x >> 6;  // 0 .. NW - 1
+  const int tg = wv % NR;           // row-tile group
+  const int ks = wv / NR;           // key slice
   const int c = lane & 15;
   const int qd = lane >> 4;
   const int b = blockIdx.y;
@@ -121,7 +138,7 @@ void attn_partial_lds(AttnParams p) {
   const int pavail = p.max_pages - start / kPage;
   int pr0 = lane < pavail ? btrow[lane] : 0;
   int pr1 = lane + 64 < pavail ? btrow[lane + 64] : 0;
-  const int row_tile0 = (it.rb * NR + wv) * RB;
+  const int row_tile0 = (it.rb * NR + tg) * RB;
   bf16x8 qf[RB][NC];
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
@@ -209,7 +226,7 @@ void attn_partial_lds(AttnParams p) {
       if (nk >= 32) {
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
-          const int im = wv + NR * k;
+          const int im = wv + NW * k;
           const bool second = im < 8 ? (im >> 2) != 0 : (im - 8) >= 4;
           const uint64_t base = (im < 8 ? kc_addr : vc_addr) + (uint64_t)(second ? p1 : p0) * page_bytes;
           const uint32_t off = im < 8 ? koff + 64u * (im & 3) : voff + ((im - 8) & 3) * slot_bytes;
@@ -218,7 +235,7 @@ void attn_partial_lds(AttnParams p) {
         return;
       }
 #pragma nounroll
-      for (int im = wv; im < 16; im += NR) {
+      for (int im = wv; im < 16; im += NW) {
         const uint16_t* src;
         if (im < 8) {
           const int kt = im >> 2, m = im & 3;
@@ -238,7 +255,7 @@ void attn_partial_lds(AttnParams p) {
     } else {
       const int j0 = 32 * (s - ncs);
 #pragma nounroll
-      for (int im = wv; im < 16; im += NR) {
+      for (int im = wv; im < 16; im += NW) {
         const uint16_t* src;
         if (im < 8) {
           const int kt = im >> 2, m = im & 3;
@@ -264,13 +281,7 @@ void attn_partial_lds(AttnParams p) {
     for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int s = 0; s < kLdsStages - 1 && s < nst; ++s) issue(s);
-
-  for (int s = 0; s < nst; ++s) {
-    const int after = min(kLdsStages - 2, nst - 1 - s);
-    wait_stage_barrier<IPW>(after);
-    if (s + kLdsStages - 1 < nst) issue(s + kLdsStages - 1);
-
+  auto compute = [&](int s) __attribute__((always_inline)) {
     const char* buf = ring + (s % kLdsStages) * kStageBytes + lane * 16;
     bf16x8 kf[2][NC];
 #pragma unroll
@@ -295,6 +306,56 @@ void attn_partial_lds(AttnParams p) {
       mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [&](int k, int e) {
         return ((vrow[k] >> (j0 + pv_key(qd, e))) & 1ull) != 0ull;
       });
+    }
+  };
+
+  if (KS > 1 && nst <= kLdsStages) {
+    // every stage in the ring at once: one wait, one barrier, then each
+    // slice reduces its own stages
+    for (int s = 0; s < nst; ++s) issue(s);
+    wait_vmem_barrier<0>();
+    for (int s = ks; s < nst; s += KS) compute(s);
+  } else {
+    for (int s = 0; s < kLdsStages - 1 && s < nst; ++s) issue(s);
+    for (int s = 0; s < nst; ++s) {
+      const int after = min(kLdsStages - 2, nst - 1 - s);
+      wait_stage_barrier<IPW>(after);
+      if (s + kLdsStages - 1 < nst) issue(s + kLdsStages - 1);
+      if (s % KS == ks) compute(s);
+    }
+  }
+
+  if constexpr (KS > 1) {
+    // slices 1 .. KS - 1 hand their states to slice 0 through the ring
+    wait_vmem_barrier<0>();  // every wave is done with the ring
+    float* sbuf = reinterpret_cast<float*>(ring);
+    auto slot = [&](int slice) { return sbuf + ((size_t)(slice * NR + tg) * kSliceStateFloats * kWave) + lane; };
+    if (ks > 0) {
+      float* d = slot(ks);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[(4 * t + e) * kWave] = st.acc[0][t][e];
+      d[32 * kWave] = st.m[0];
+      d[33 * kWave] = st.l[0];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (ks > 0) return;
+#pragma unroll
+    for (int o = 1; o < KS; ++o) {
+      const float* d = slot(o);
+      const float mo = d[32 * kWave];
+      const float lo = d[33 * kWave];
+      const float mm = fmaxf(st.m[0], mo);
+      const float mu = mm == neg_inf() ? 0.f : mm;
+      const float a = fast_exp2(st.m[0] - mu);
+      const float bo = fast_exp2(mo - mu);
+      st.l[0] = st.l[0] * a + lo * bo;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.acc[0][t][e] = st.acc[0][t][e] * a + d[(4 * t + e) * kWave] * bo;
+      st.m[0] = mm;
     }
   }
 

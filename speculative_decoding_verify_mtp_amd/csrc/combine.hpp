@@ -39,7 +39,7 @@ __device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamPa
   // first: for the split layout, the accumulators of the first 32 splits of
   // the launch-wide split count (splits past this row's count are dropped
   // by selection, never by a zero weight: stale workspace may hold NaN).
-  constexpr int kBatch = 8;  // splits per 16-lane group in flight
+  constexpr int kBatch = kCombineFast / 4;  // splits per 16-lane group in flight
   size_t base0 = 0, sstride0 = 0;
   if constexpr (!kStream) {
     base0 = (((size_t)b * p.max_splits) * p.Hkv + kvh) * (size_t)p.R + rho;

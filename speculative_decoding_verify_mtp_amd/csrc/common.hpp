@@ -22,6 +22,10 @@ __device__ unsigned int g_status;
 
 __device__ __forceinline__ void raise_status(unsigned bits) { atomicOr(&g_status, bits); }
 
+// Splits of an output row whose accumulators the combine requests in its
+// first batch (four 16-lane groups of kCombineFast / 4).
+constexpr int kCombineFast = 32;
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
 

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "attn_stream.hpp"
 #include "attn_valu.hpp"
 #include "common.hpp"
@@ -42,7 +44,8 @@ struct Plan {
   bool mfma;       // bf16 with >= 16 rows per KV head
   int g, R;        // group size, rows per KV head (W * g)
   int RB;          // MFMA row tiles per wave (1, 2 or 4)
-  int NR;          // waves per workgroup (LDS kernel; 1 wave per item otherwise)
+  int NR;          // row-tile groups (waves) per workgroup (LDS kernel; 1 wave per item otherwise)
+  int KS;          // key slices per workgroup (LDS kernel: NR * KS waves)
   int nRB;         // row blocks (MFMA) or row chunks (VALU) per KV head
   int S;           // committed tokens per split
   int max_splits;  // splits of the longest context
@@ -84,6 +87,7 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
   pl.R = s.W * pl.g;
   pl.mfma = nested || (s.dtype == MTP_BF16 && pl.R >= 16);
   pl.NR = 1;
+  pl.KS = 1;
   const int tiles = (pl.R + 15) / 16;
   if (nested) {
     pl.kernel = kMfmaNested;
@@ -122,13 +126,27 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
     S = S < floor_rows ? floor_rows : S;
     pl.S = S < kMinSplit ? kMinSplit : (S > kMaxSplit ? kMaxSplit : S);
   }
+  pl.nts = (s.W + 31) / 32;
+  const bool stream_shape = pl.kernel == kMfmaLds && s.B >= kStreamMinB && s.B <= kStreamMaxB;
+  // Per-split LDS kernel with one or two row tiles per workgroup: two key
+  // slices (each wave reduces half of the stages) when every stage of a split
+  // fits the ring.  The automatic split then also grows, within the ring, until
+  // a row has at most kCombineFast splits (the combine's first batch), which
+  // halves the partial writes and drops a combine round trip.
+  const int ks_cap = 32 * (kLdsStages - pl.nts);  // longest split whose stages all fit the ring
+  if (pl.kernel == kMfmaLds && !stream_shape && pl.RB == 1 && pl.NR <= 2) {
+    if (s.split_tokens == 0 && pl.S < ks_cap) {
+      const long want = ((long)(s.max_ctx_len + kCombineFast - 1) / kCombineFast + 31) / 32 * 32;
+      pl.S = (int)std::max<long>(pl.S, std::min<long>(ks_cap, want));
+    }
+    if (pl.S <= ks_cap) pl.KS = 2;
+  }
   pl.max_splits = s.max_ctx_len > 0 ? (s.max_ctx_len + pl.S - 1) / pl.S : 1;
   pl.G = 0;
-  pl.nts = (s.W + 31) / 32;
   pl.nseg = s.Hkv * pl.nRB;
   pl.rows_block = 16 * pl.NR * pl.RB;
   size_t rows = (size_t)s.B * pl.max_splits * s.Hkv * pl.R;
-  if (pl.kernel == kMfmaLds && s.B >= kStreamMinB && s.B <= kStreamMaxB) {
+  if (stream_shape) {
     // stage count bound from max_ctx_len; the device splits the true count
     const long seg_stages = (long)(s.max_ctx_len + 31) / 32 + pl.nts;
     const long upper = (long)s.B * pl.nseg * seg_stages;

@@ -118,7 +118,9 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     wave of 1, 2 or 4 row tiles per row block), everything else in chunks of
     4 rows; the automatic split is the power of two giving about 1024
     workgroups (LDS kernel) or 2048 waves (the others), at least twice the
-    rows of an item, clamped to [64, 2048] tokens."""
+    rows of an item, clamped to [64, 2048] tokens; the per-split D=128 kernel
+    with one or two row tiles raises it, up to what its ring holds, to at
+    most 32 splits per row."""
     g = Hq // Hkv
     R = W * g
     tiles = (R + 15) // 16
@@ -148,6 +150,14 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
         S = min(max(S, 64), 2048)
     else:
         S = split
+    stream = dtype == lib.MTP_BF16 and R >= 16 and D == 128 and 8 <= B <= 1024
+    if dtype == lib.MTP_BF16 and R >= 16 and D == 128 and not stream and rb == 1 and nr <= 2:
+        # key slices: a split whose stages all fit the 5-stage ring; the
+        # automatic split grows (within it) to at most 32 splits per row
+        cap = 32 * (5 - (W + 31) // 32)
+        if split == 0 and S < cap:
+            want = -(-(-(-max_ctx // 32)) // 32) * 32
+            S = max(S, min(cap, want))
     ns = -(-max_ctx // S) if max_ctx > 0 else 1
     rows = B * ns * Hkv * R
     seg = 0

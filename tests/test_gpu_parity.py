@@ -63,7 +63,7 @@ def test_attention_matches_oracle_small(wl):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
 
 
-@pytest.mark.parametrize("split", [32, 64, 96, 2048])
+@pytest.mark.parametrize("split", [32, 64, 96, 128, 2048])
 def test_split_size_does_not_change_the_result(split):
     wl = W_("splits", B=3, Hq=16, Hkv=4, W=8, ctx_lo=1, ctx_hi=700, masks="mixed")
     inp = gpu_inputs(wl, 3)
