@@ -1,11 +1,17 @@
 // Stream-K verify attention, D = 128, bf16 MFMA, K/V through an LDS ring.
 //
-// The work of one launch is the flat list of 32-key stages of every segment
-// sigma = (sequence b, KV head, row block), in that order: segment sigma of
-// sequence b has ceil(L_b / 32) committed stages followed by ceil(W / 32)
-// in-block stages.  A persistent grid of G workgroups cuts that list into G
-// equal contiguous ranges, so every workgroup streams the same number of
-// stages whatever the mix of context lengths, and no workgroup is empty.
+// The work of one launch is, per KV head, the flat list of 32-key stages of
+// every segment (sequence b, row block) of that head, in that order: the
+// segment of sequence b has ceil(L_b / 32) committed stages followed by
+// ceil(W / 32) in-block stages.  The lists of all KV heads have the same
+// length.  A persistent grid of G = Hkv * G' workgroups gives each head G'
+// workgroups, which cut its list into G' equal contiguous ranges: every
+// workgroup streams the same number of stages whatever the mix of context
+// lengths, and no workgroup is empty.  Workgroup w serves head w % Hkv and
+// range w / Hkv, so the Hkv workgroups of one range are dispatched together
+// and walk the same pages at the same time, each reading its head's slice of
+// every token slot: the DRAM rows they open are shared (measured: scattering
+// the heads of a page over the dispatch order costs about 5% of the stream).
 //
 // A workgroup walks its range in runs: a run is at most kRunStages stages of
 // one segment, covered by one window of page indices held in four registers
@@ -15,11 +21,13 @@
 // state carries over runs of the same segment; when the segment (or the
 // range) ends, the workgroup writes one partial "piece".
 //
-// Piece ids: a piece is a pair (workgroup w, segment sigma) with w's range
-// overlapping sigma.  Walking the list, each step to the next piece raises w,
-// sigma or both by one, so w + sigma is unique and below G + #segments.  The
-// workgroup that holds a segment's first stage records (first piece id, piece
-// count) for the combine.
+// Piece ids: within one head, a piece is a pair (range r, segment s) with
+// range r overlapping segment s.  Walking the head's list, each step to the
+// next piece raises r, s or both by one, so r + s is unique and below
+// G' + B * row_blocks; head k's pieces take ids k * (G' + B * row_blocks) +
+// r + s.  The pieces of one segment therefore have consecutive ids.  The
+// workgroup that holds a segment's first stage records (first piece id,
+// piece count) for the combine.
 #pragma once
 
 #include "attn_lds.hpp"
@@ -54,14 +62,14 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
   __shared__ __attribute__((aligned(16))) char ring[NS * kStageBytes];
   __shared__ int s_pref[kStreamMaxB + 1];
 
-  const int wg = (int)blockIdx.x;  // this workgroup's range index
+  const int wg = (int)blockIdx.x;
   const int G = (int)gridDim.x;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int c = lane & 15;
   const int qd = lane >> 4;
 
-  // ---- stage prefix over sequences: s_pref[b] = stages of sequences < b
+  // ---- stage prefix over sequences of one head's list: s_pref[b] = stages of sequences < b
   if (wv == 0) {
     int run = 0;
     for (int b0 = 0; b0 < p.B; b0 += kWave) {
@@ -69,7 +77,7 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
       int n = 0;
       if (bb < p.B) {
         const int L = p.ctx_lens[bb];
-        if (L >= 0 && L <= p.max_ctx) n = ((L + 31) / 32 + sp.nts) * sp.nseg;
+        if (L >= 0 && L <= p.max_ctx) n = ((L + 31) / 32 + sp.nts) * p.nRB;
       }
       int x = n;
 #pragma unroll
@@ -84,8 +92,12 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
   }
   __syncthreads();
   const int total = s_pref[p.B];
-  const int T = (total + G - 1) / G;
-  int g = wg * T;
+  const int Gh = G / p.Hkv;          // ranges per head (the host makes G a multiple of Hkv)
+  const int gi = wg / p.Hkv;         // this workgroup's range
+  const int kvh = wg - gi * p.Hkv;   // and head
+  const int piece0 = kvh * (Gh + p.B * p.nRB) + gi;
+  const int T = (total + Gh - 1) / Gh;
+  int g = gi * T;
   const int g_end = min(g + T, total);
   if (g >= g_end) return;  // uniform over the workgroup
 
@@ -111,15 +123,14 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
       else hi = mid;
     }
     const int b = lo;
-    const int nb = (s_pref[b + 1] - s_pref[b]) / sp.nseg;
+    const int nb = (s_pref[b + 1] - s_pref[b]) / p.nRB;
     const int ncs = nb - sp.nts;
     const int off = g - s_pref[b];
-    const int seg = off / nb;
-    const int i0 = off - seg * nb;
-    const int kvh = seg / p.nRB;
-    const int rb = seg - kvh * p.nRB;
-    const int sigma = b * sp.nseg + seg;
-    const int seg_end_g = s_pref[b] + (seg + 1) * nb;
+    const int rb = off / nb;
+    const int i0 = off - rb * nb;
+    const int lsig = b * p.nRB + rb;  // segment index in this head's list
+    const int sigma = b * sp.nseg + kvh * p.nRB + rb;
+    const int seg_end_g = s_pref[b] + (rb + 1) * nb;
     const int i1 = min(nb, i0 + min(g_end - g, kRunStages));
     const int L = p.ctx_lens[b];
 
@@ -154,8 +165,8 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
         vrow[k] = 0;
       }
       if (i0 == 0 && threadIdx.x == 0) {
-        sp.seg_info[2 * sigma] = wg + sigma;
-        sp.seg_info[2 * sigma + 1] = (seg_end_g - 1) / T - wg + 1;
+        sp.seg_info[2 * sigma] = piece0 + lsig;
+        sp.seg_info[2 * sigma + 1] = (seg_end_g - 1) / T - gi + 1;
       }
     }
 
@@ -300,7 +311,7 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
           for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{qnan(), qnan(), qnan(), qnan()};
         }
       }
-      const size_t piece = (size_t)wg + sigma;
+      const size_t piece = (size_t)piece0 + lsig;
 #pragma unroll
       for (int k = 0; k < RB; ++k) {
         float l = st.l[k];

@@ -31,8 +31,8 @@ constexpr int kMaxSplit = 2048;
 enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3, kMfmaNested = 4 };
 
 // Stream kernel: persistent grid sized for gfx950's 256 CUs (two workgroups
-// per CU at one row tile per wave, one at two), each workgroup streaming at
-// least kMinStreamStages stages.
+// per CU at one row tile per wave, one at two) and rounded down to a multiple
+// of Hkv, each workgroup streaming at least kMinStreamStages stages.
 constexpr int kCUs = 256;
 constexpr long kMinStreamStages = 2;
 // A handful of sequences is balanced by the split plan already, and the
@@ -150,13 +150,17 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
     // stage count bound from max_ctx_len; the device splits the true count
     const long seg_stages = (long)(s.max_ctx_len + 31) / 32 + pl.nts;
     const long upper = (long)s.B * pl.nseg * seg_stages;
-    if (upper < (1L << 30)) {
+    if (upper < (1L << 30) && s.Hkv <= 65535) {
       pl.kernel = kMfmaStream;
+      // G = Hkv * Gh: each KV head's list is cut into Gh ranges
       const long slots = (long)kCUs * (pl.RB == 1 ? 2 : 1);
-      long per = s.split_tokens > 0 ? s.split_tokens / 32 : kMinStreamStages;
-      long G = (upper + per - 1) / per;
-      if (s.split_tokens == 0 && G > slots) G = slots;
-      pl.G = (int)(G < 1 ? 1 : (G > 65535 ? 65535 : G));
+      const long per = s.split_tokens > 0 ? s.split_tokens / 32 : kMinStreamStages;
+      const long upper_h = upper / s.Hkv;
+      long Gh = (upper_h + per - 1) / per;
+      const long slots_h = slots / s.Hkv > 0 ? slots / s.Hkv : 1;
+      if (s.split_tokens == 0 && Gh > slots_h) Gh = slots_h;
+      const long max_h = 65535 / s.Hkv;
+      pl.G = (int)((Gh < 1 ? 1 : (Gh > max_h ? max_h : Gh)) * s.Hkv);
       rows = ((size_t)pl.G + (size_t)s.B * pl.nseg) * pl.rows_block;
     }
   }

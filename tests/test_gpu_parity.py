@@ -106,6 +106,24 @@ def test_stream_work_split_does_not_change_the_result(split):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"stream split {split}")
 
 
+STREAM_HEADS = [
+    W_("stream_hkv5", B=9, Hq=20, Hkv=5, W=8, ctx_lo=0, ctx_hi=1500, masks="chain"),
+    W_("stream_hkv1_rb2", B=8, Hq=16, Hkv=1, W=16, ctx_lo=40, ctx_hi=900, masks="mixed"),
+    W_("stream_hkv16", B=10, Hq=32, Hkv=16, W=8, ctx_lo=0, ctx_hi=700, masks="tree"),
+]
+
+
+@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("wl", STREAM_HEADS, ids=[w.name for w in STREAM_HEADS])
+def test_stream_ranges_per_kv_head(wl, split):
+    """The stream grid is Hkv workgroups per range: head counts that do and
+    do not divide the slot count, one or two row blocks per head."""
+    inp = gpu_inputs(wl, 17)
+    out, lse = run_attn(inp, split_tokens=split)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"{wl.name} split {split}")
+
+
 def test_loose_max_ctx_len_bound():
     """max_ctx_len only sizes the split plan; a loose bound gives the same result."""
     wl = W_("loose", B=2, Hq=8, Hkv=2, W=8, ctx_lo=10, ctx_hi=300, masks="tree")
