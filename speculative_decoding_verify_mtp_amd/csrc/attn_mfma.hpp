@@ -195,15 +195,17 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
   const int b = blockIdx.y;
   const Item it = decode_item(blockIdx.x * 4 + (threadIdx.x >> 6), p);
   if (it.split >= p.max_splits) return;
-  const int mkind = p.mask_kind[b];  // loaded with the context length
-  const int mid = lane_mask_id(p, b, lane);
-  const int L = p.ctx_lens[b];
-  if (L < 0 || L > p.max_ctx) return;  // reported by the combine
-  const int ns = num_splits(L, p.S);
-  if (it.split >= ns) return;
   const int start = it.split * p.S;
-  const int end = min(L, start + p.S);
-  const bool last = it.split == ns - 1;
+
+  // Loads that do not depend on the context length go out together with it:
+  // the split's page indices (held in two registers per lane: lane i has
+  // entries i and 64 + i; a split spans at most 128 pages; bounded by the
+  // block table, not by the context) and the Q operands.
+  const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
+  const int pbase = start >> 4;
+  const int pavail = p.max_pages - pbase;
+  const int pr0 = lane < pavail ? btrow[pbase + lane] : 0;
+  const int pr1 = lane + 64 < pavail ? btrow[pbase + lane + 64] : 0;
 
   const uint16_t* qbase = static_cast<const uint16_t*>(p.q);
   const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache) + (size_t)it.kvh * D;
@@ -228,6 +230,15 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
     }
   }
 
+  const int mkind = p.mask_kind[b];
+  const int mid = lane_mask_id(p, b, lane);
+  const int L = p.ctx_lens[b];
+  if (L < 0 || L > p.max_ctx) return;  // reported by the combine
+  const int ns = num_splits(L, p.S);
+  if (it.split >= ns) return;
+  const int end = min(L, start + p.S);
+  const bool last = it.split == ns - 1;
+
   MfmaState<D, RB> st;
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
@@ -238,15 +249,9 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
   }
 
   // Committed keys [start, end), 32 per step (two pages; start is a multiple
-  // of 32).  The split's page indices are held in two registers per lane
-  // (lane i: entries i and 64 + i; a split spans at most 128 pages), and the
-  // K/V rows of the next step are requested before the current step is
-  // reduced: one memory round trip per step, overlapped with the compute.
-  const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
-  const int pbase = start >> 4;
-  const int pavail = p.max_pages - pbase;
-  const int pr0 = lane < pavail ? btrow[pbase + lane] : 0;
-  const int pr1 = lane + 64 < pavail ? btrow[pbase + lane + 64] : 0;
+  // of 32).  The K/V rows of the next step are requested before the current
+  // step is reduced: one memory round trip per step, overlapped with the
+  // compute.
   bool bad = false;
   struct Step {
     bf16x8 kf[2][NC];

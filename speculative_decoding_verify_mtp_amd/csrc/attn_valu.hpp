@@ -56,20 +56,18 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
   const int b = blockIdx.y;
   const Item it = decode_item(blockIdx.x * 4 + (threadIdx.x >> 6), p);
   if (it.split >= p.max_splits) return;
-  const int L = p.ctx_lens[b];
-  if (L < 0 || L > p.max_ctx) return;
-  const int ns = num_splits(L, p.S);
-  if (it.split >= ns) return;
   const int start = it.split * p.S;
-  const int end = min(L, start + p.S);
-  const bool last = it.split == ns - 1;
-  // the split's page indices, lane i holding entries i and 64 + i (a split
-  // spans at most 128 pages)
+  // Loads that do not depend on the context length go out together with it:
+  // the split's page indices (lane i holding entries i and 64 + i; a split
+  // spans at most 128 pages; bounded by the block table, not by the
+  // context), the mask description and, below, Q.
   const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
   const int pbase = start >> 4;
   const int pavail = p.max_pages - pbase;
   const int pr0 = lane < pavail ? btrow[pbase + lane] : 0;
   const int pr1 = lane + 64 < pavail ? btrow[pbase + lane + 64] : 0;
+  const int mkind = p.mask_kind[b];
+  const int mid = lane_mask_id(p, b, lane);
 
   const T* qbase = static_cast<const T*>(p.q);
   const T* kc = static_cast<const T*>(p.k_cache) + (size_t)it.kvh * D + sub * 16;
@@ -93,6 +91,13 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
     }
   }
 
+  const int L = p.ctx_lens[b];
+  if (L < 0 || L > p.max_ctx) return;
+  const int ns = num_splits(L, p.S);
+  if (it.split >= ns) return;
+  const int end = min(L, start + p.S);
+  const bool last = it.split == ns - 1;
+
   // In-block visibility rows of this item's rows (last split only).
   int ntail = 0;
   uint64_t vrow[RC];
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
   if (last) {
     bool ok;
     const uint64_t vnode =
-        node_visibility(p.mask_kind[b], lane_mask_id(p, b, lane), p.W, p.lookback, lane, ok);
+        node_visibility(mkind, mid, p.W, p.lookback, lane, ok);
     if (ok) {
       ntail = p.W;
 #pragma unroll
