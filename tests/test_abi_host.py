@@ -162,14 +162,15 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     rows = B * ns * Hkv * R
     seg = 0
     if dtype == lib.MTP_BF16 and R >= 16 and D == 128 and 8 <= B <= 1024:
-        # stream kernel: G persistent workgroups, pieces <= G + segments
+        # stream kernel: G = Hkv * Gh persistent workgroups (Gh ranges per KV
+        # head), pieces <= G + segments
         nseg = Hkv * nrb
         upper = B * nseg * (-(-max_ctx // 32) + -(-W // 32))
         per = split // 32 if split else 2
-        G = -(-upper // per)
+        Gh = -(-(upper // Hkv) // per)
         if not split:
-            G = min(G, 256 * (2 if rb == 1 else 1))
-        G = max(1, min(G, 65535))
+            Gh = min(Gh, max(1, 256 * (2 if rb == 1 else 1) // Hkv))
+        G = max(1, min(Gh, 65535 // Hkv)) * Hkv
         rows = (G + B * nseg) * rows_item
         seg = B * nseg * 8
     acc = rows * D * 4
@@ -191,6 +192,8 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     dict(B=1100, W=4, Hq=4, Hkv=1, D=128, dtype=1, max_ctx=300),
     dict(B=3, W=33, Hq=8, Hkv=2, D=128, dtype=1, max_ctx=5000, split=256),
     dict(B=9, W=33, Hq=8, Hkv=2, D=128, dtype=1, max_ctx=5000, split=256),
+    dict(B=9, W=8, Hq=20, Hkv=5, D=128, dtype=1, max_ctx=1500),
+    dict(B=10, W=8, Hq=32, Hkv=16, D=128, dtype=1, max_ctx=700, split=64),
 ])
 def test_workspace_follows_the_split_plan(L, kw):
     s = lib.VerifyShape(kw["B"], kw["W"], kw["Hq"], kw["Hkv"], kw["D"], 10,
