@@ -489,16 +489,19 @@ def main() -> int:
     ap.add_argument("--write-traffic", metavar="WORKLOAD", default=None,
                     help="only write profiles/traffic_WORKLOAD.json from rocprofv3 counter "
                          "CSVs under --ctr-dir (no GPU needed), then exit")
-    ap.add_argument("--ctr-dir", default="gpurun_out/ctr")
+    ap.add_argument("--ctr-dir", default=None,
+                    help="directory holding the counter runs (required with --write-traffic)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.write_traffic:
+        if not args.ctr_dir:
+            ap.error("--write-traffic needs --ctr-dir")
         return write_traffic(args.write_traffic, args.ctr_dir)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the verify step is measured on one "
-              "GPU's share); --gpus must be 1", file=sys.stderr)
+        print("bench.py: the verify step is measured on one GPU (its share of a sharded "
+              "batch is the same kernel at its own shape); --gpus must be 1", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
