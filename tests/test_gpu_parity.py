@@ -110,6 +110,8 @@ STREAM_HEADS = [
     W_("stream_hkv5", B=9, Hq=20, Hkv=5, W=8, ctx_lo=0, ctx_hi=1500, masks="chain"),
     W_("stream_hkv1_rb2", B=8, Hq=16, Hkv=1, W=16, ctx_lo=40, ctx_hi=900, masks="mixed"),
     W_("stream_hkv16", B=10, Hq=32, Hkv=16, W=8, ctx_lo=0, ctx_hi=700, masks="tree"),
+    # more KV heads than persistent workgroups: one range per head
+    W_("stream_hkv600", B=8, Hq=600, Hkv=600, W=16, ctx_lo=0, ctx_hi=100, masks="chain"),
 ]
 
 
