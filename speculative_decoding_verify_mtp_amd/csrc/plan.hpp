@@ -25,7 +25,7 @@ using namespace mtpv;
 // bytes, then stays below half of the K/V it reads, split x 4D bytes).
 constexpr long kTargetWorkgroups = 1024;
 constexpr long kTargetWaves = 2048;
-constexpr int kMinSplit = 64;
+constexpr int kMinSplit = 32;  // one 32-key stage: short contexts are latency-bound
 constexpr int kMaxSplit = 2048;
 
 enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3, kMfmaNested = 4 };

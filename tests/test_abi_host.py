@@ -118,7 +118,7 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     wave of 1, 2 or 4 row tiles per row block), everything else in chunks of
     4 rows; the automatic split is the power of two giving about 1024
     workgroups (LDS kernel) or 2048 waves (the others), at least twice the
-    rows of an item, clamped to [64, 2048] tokens; the per-split D=128 kernel
+    rows of an item, clamped to [32, 2048] tokens; the per-split D=128 kernel
     with one or two row tiles raises it, up to what its ring holds, to at
     most 32 splits per row."""
     g = Hq // Hkv
@@ -147,7 +147,7 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     if split == 0:
         work = B * Hkv * nrb * max(max_ctx, 1)
         S = max(pow2_ceil(-(-work // items)), pow2_ceil(2 * rows_item))
-        S = min(max(S, 64), 2048)
+        S = min(max(S, 32), 2048)
     else:
         S = split
     stream = dtype == lib.MTP_BF16 and R >= 16 and D == 128 and 8 <= B <= 1024
