@@ -326,7 +326,17 @@ void attn_partial_lds(AttnParams p) {
   }
 
   if constexpr (KS > 1) {
-    // slices 1 .. KS - 1 hand their states to slice 0 through the ring
+    // Slices 1 .. KS - 1 hand their states to slice 0 through the ring.
+    // Slice 0 merges them and lays its rows out row-major in the ring (row
+    // pitch D + 4 floats, so the 16 rows a store instruction spans fall in
+    // different banks); then every wave of the workgroup stores whole rows,
+    // 1 KB per store instruction, instead of slice 0 storing 16-byte pieces
+    // of 16 rows per instruction.  The row image (NR * 16 rows) ends below
+    // the slice states (which start at NR * kSliceStateFloats floats per
+    // lane), so slice 0 may write rows while another of its waves still
+    // reads states.
+    constexpr int kPitch = D + 4;
+    static_assert(16 * kPitch <= kSliceStateFloats * kWave, "row image below the slice states");
     wait_vmem_barrier<0>();  // every wave is done with the ring
     float* sbuf = reinterpret_cast<float*>(ring);
     auto slot = [&](int slice) { return sbuf + ((size_t)(slice * NR + tg) * kSliceStateFloats * kWave) + lane; };
@@ -340,23 +350,57 @@ void attn_partial_lds(AttnParams p) {
       d[33 * kWave] = st.l[0];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (ks > 0) return;
+    const size_t item_row = (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R;
+    if (ks == 0) {
 #pragma unroll
-    for (int o = 1; o < KS; ++o) {
-      const float* d = slot(o);
-      const float mo = d[32 * kWave];
-      const float lo = d[33 * kWave];
-      const float mm = fmaxf(st.m[0], mo);
-      const float mu = mm == neg_inf() ? 0.f : mm;
-      const float a = fast_exp2(st.m[0] - mu);
-      const float bo = fast_exp2(mo - mu);
-      st.l[0] = st.l[0] * a + lo * bo;
+      for (int o = 1; o < KS; ++o) {
+        const float* d = slot(o);
+        const float mo = d[32 * kWave];
+        const float lo = d[33 * kWave];
+        const float mm = fmaxf(st.m[0], mo);
+        const float mu = mm == neg_inf() ? 0.f : mm;
+        const float a = fast_exp2(st.m[0] - mu);
+        const float bo = fast_exp2(mo - mu);
+        st.l[0] = st.l[0] * a + lo * bo;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.acc[0][t][e] = st.acc[0][t][e] * a + d[(4 * t + e) * kWave] * bo;
-      st.m[0] = mm;
+          for (int e = 0; e < 4; ++e) st.acc[0][t][e] = st.acc[0][t][e] * a + d[(4 * t + e) * kWave] * bo;
+        st.m[0] = mm;
+      }
+      if (bad) {
+        if (threadIdx.x == 0) raise_status(MTP_DEV_BAD_PAGE);
+        st.m[0] = qnan();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) st.acc[0][t] = f32x4{qnan(), qnan(), qnan(), qnan()};
+      }
+      const float l = rows4_sum(st.l[0]);
+      const int rho = row_tile0 * 16 + c;
+      if (qd == 0 && rho < p.R) {
+        p.part_ml[2 * (item_row + rho)] = st.m[0];
+        p.part_ml[2 * (item_row + rho) + 1] = l;
+      }
+      // float4 j of lane (c, qd) holds row c, d = qd * D / 4 + 4 j .. + 4
+      float* rowp = sbuf + (size_t)(tg * 16 + c) * kPitch + qd * (D / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int t = 0; t < NT; t += 4)
+          *reinterpret_cast<float4*>(rowp + e * (D / 16) + t) =
+              make_float4(st.acc[0][t][e], st.acc[0][t + 1][e], st.acc[0][t + 2][e], st.acc[0][t + 3][e]);
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int row0 = it.rb * NR * 16;  // first row of this workgroup's row block
+    constexpr int kVecs = NR * 16 * (D / 4);
+#pragma unroll
+    for (int f = threadIdx.x; f < kVecs; f += 64 * NW) {
+      const int row = f / (D / 4);
+      const int col = f - row * (D / 4);
+      if (row0 + row < p.R)
+        *reinterpret_cast<float4*>(p.part_acc + (item_row + row0 + row) * D + col * 4) =
+            *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4);
+    }
+    return;
   }
 
   if (bad) {
