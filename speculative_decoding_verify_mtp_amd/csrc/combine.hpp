@@ -3,11 +3,13 @@
 // lse = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s).  Sequences with a malformed
 // mask or context length get NaN rows.
 //
-// One wave per row, `rows` rows per workgroup (waves past them idle).  Pass 1 spreads the splits over the lanes (one split per
-// lane) for M and the denominator.  Pass 2 splits the wave into four groups of
-// sixteen lanes: group q takes splits q, q+4, ..., each lane D/16 consecutive
-// accumulators, so every load is 16-byte wide and many are in flight; the
-// four group sums are folded with two shuffles.
+// Split layout (combine_rows): one wave per row, `rows` rows per workgroup
+// (waves past them idle).  Pass 1 spreads the splits over the lanes (one
+// split per lane) for M and the denominator.  Pass 2 splits the wave into
+// four groups of sixteen lanes: group q takes splits q, q+4, ..., each lane
+// D/16 consecutive accumulators, so every load is 16-byte wide and many are
+// in flight; the four group sums are folded with two shuffles.
+// Stream layout (combine_rows_stream): four rows per wave, see there.
 #pragma once
 
 #include "accept_commit.hpp"
@@ -16,12 +18,9 @@
 
 namespace mtpv {
 
-// kStream = false: partials of the split kernels, [B, splits, Hkv, R] rows.
-// kStream = true : pieces of the stream kernel, [pieces, rows_block] rows,
-//                  located through the segment table.
-template <int D, bool kStream>
-__device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamParams& sp, unsigned block,
-                                             int rows) {
+// Partials of the split kernels, [B, splits, Hkv, R] rows.
+template <int D>
+__device__ __forceinline__ void combine_rows(const AttnParams& p, unsigned block, int rows) {
   constexpr int VPL = D / 16;  // accumulators per lane per split
   const int lane = threadIdx.x & 63;
   const int gq = lane >> 4, gl = lane & 15;
@@ -36,30 +35,25 @@ __device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamPa
   const int rho = w * p.g + (h - kvh * p.g);
 
   // Loads that need neither the context length nor the split states go out
-  // first: for the split layout, the accumulators of the first 32 splits of
-  // the launch-wide split count (splits past this row's count are dropped
+  // first: the accumulators of the first kCombineFast splits of the
+  // launch-wide split count (splits past this row's count are dropped
   // by selection, never by a zero weight: stale workspace may hold NaN).
   constexpr int kBatch = kCombineFast / 4;  // splits per 16-lane group in flight
-  size_t base0 = 0, sstride0 = 0;
-  if constexpr (!kStream) {
-    base0 = (((size_t)b * p.max_splits) * p.Hkv + kvh) * (size_t)p.R + rho;
-    sstride0 = (size_t)p.Hkv * p.R;
-  }
+  const size_t base = (((size_t)b * p.max_splits) * p.Hkv + kvh) * (size_t)p.R + rho;
+  const size_t sstride = (size_t)p.Hkv * p.R;
   float4 v[kBatch][VPL / 4];
   float m_spec = neg_inf(), l_spec = 0.f;  // split state of split `lane`
-  if constexpr (!kStream) {
-    if (lane < p.max_splits) {
-      m_spec = p.part_ml[2 * (base0 + lane * sstride0)];
-      l_spec = p.part_ml[2 * (base0 + lane * sstride0) + 1];
-    }
-    const int nspec = p.max_splits < 4 * kBatch ? p.max_splits : 4 * kBatch;
+  if (lane < p.max_splits) {
+    m_spec = p.part_ml[2 * (base + lane * sstride)];
+    l_spec = p.part_ml[2 * (base + lane * sstride) + 1];
+  }
+  const int nspec = p.max_splits < 4 * kBatch ? p.max_splits : 4 * kBatch;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int sl = 4 * u + gq < nspec ? 4 * u + gq : 0;
-      const float4* src = reinterpret_cast<const float4*>(p.part_acc + (base0 + sl * sstride0) * D + gl * VPL);
+  for (int u = 0; u < kBatch; ++u) {
+    const int sl = 4 * u + gq < nspec ? 4 * u + gq : 0;
+    const float4* src = reinterpret_cast<const float4*>(p.part_acc + (base + sl * sstride) * D + gl * VPL);
 #pragma unroll
-      for (int j = 0; j < VPL / 4; ++j) v[u][j] = src[j];
-    }
+    for (int j = 0; j < VPL / 4; ++j) v[u][j] = src[j];
   }
 
   const int L = p.ctx_lens[b];
@@ -74,40 +68,9 @@ __device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamPa
     if (p.lse != nullptr && lane == 0) p.lse[row] = qnan();
     return;
   }
-  int ns;
-  size_t base, sstride;
-  if constexpr (kStream) {
-    const int rb = rho / sp.rows_block;
-    const int sigma = b * sp.nseg + kvh * p.nRB + rb;
-    ns = sp.seg_info[2 * sigma + 1];
-    base = (size_t)sp.seg_info[2 * sigma] * sp.rows_block + (rho - rb * sp.rows_block);
-    sstride = (size_t)sp.rows_block;
-  } else {
-    ns = num_splits(L, p.S);
-    base = (((size_t)b * p.max_splits) * p.Hkv + kvh) * (size_t)p.R + rho;
-    sstride = (size_t)p.Hkv * p.R;
-  }
-
-  // Stream layout: the pieces are known now; their accumulators are requested
-  // before the split states come back (they do not depend on the max).
+  const int ns = num_splits(L, p.S);
   const int nfast = ns < 4 * kBatch ? ns : 4 * kBatch;
-  if constexpr (kStream) {
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int sl = 4 * u + gq < nfast ? 4 * u + gq : 0;
-      const float4* src = reinterpret_cast<const float4*>(p.part_acc + (base + sl * sstride) * D + gl * VPL);
-#pragma unroll
-      for (int j = 0; j < VPL / 4; ++j) v[u][j] = src[j];
-    }
-  }
 
-  // pass 1: reference max and denominator, one split per lane
-  if constexpr (kStream) {
-    if (lane < ns) {
-      m_spec = p.part_ml[2 * (base + lane * sstride)];
-      l_spec = p.part_ml[2 * (base + lane * sstride) + 1];
-    }
-  }
   const bool have = lane < ns;
   float M = have ? m_spec : neg_inf();
   for (int s = lane + kWave; s < ns; s += kWave) M = fmaxf(M, p.part_ml[2 * (base + s * sstride)]);
@@ -190,14 +153,130 @@ __device__ __forceinline__ void combine_rows(const AttnParams& p, const StreamPa
   if (p.lse != nullptr && lane == 0) p.lse[row] = (M + log2f(den)) * kLn2;
 }
 
+// Stream layout: a row has few pieces (a segment spans one to a few
+// ranges), so one row per wave would leave most lanes idle and the rows would
+// take many rounds of waves, each paying the two dependent round trips
+// (segment table, then pieces).  Here each 16-lane group of a wave takes its
+// own row (rows 4 r .. 4 r + 3 of the flat [B, W, Hq] order), each lane D/16
+// consecutive columns, and folds the row's pieces online, four pieces' loads
+// in flight at a time.  Pieces past the row's count are dropped by selection.
+template <int D>
+__device__ __forceinline__ void combine_rows_stream(const AttnParams& p, const StreamParams& sp,
+                                                    unsigned block, unsigned nblocks, int waves) {
+  constexpr int VPL = D / 16;  // columns per lane
+  const int lane = threadIdx.x & 63;
+  const int gq = lane >> 4, gl = lane & 15;
+  const int wv = threadIdx.x >> 6;
+  if (wv >= waves) return;  // uniform over the wave
+  const size_t nrows = (size_t)p.B * p.W * p.Hq;
+  // A wave takes rows 4 (i + k n) .. + 3 for k = 0, 1, ... (n = combine waves
+  // of the launch): few workgroups, each kept busy, rather than one
+  // workgroup per handful of rows (dispatching and retiring workgroups of the
+  // step's finish launch costs more than their work).
+  const size_t n = (size_t)nblocks * waves;
+  for (size_t row0 = ((size_t)block * waves + wv) * 4; row0 < nrows; row0 += 4 * n) {
+    const bool live = row0 + gq < nrows;
+    const size_t row = live ? row0 + gq : row0;  // a group past the end repeats row 0, stores nothing
+    const int h = (int)(row % p.Hq);
+    const size_t bw = row / p.Hq;
+    const int w = (int)(bw % p.W);
+    const int b = (int)(bw / p.W);
+    const int kvh = h / p.g;
+    const int rho = w * p.g + (h - kvh * p.g);
+    const int rb = rho / sp.rows_block;
+    const int sigma = b * sp.nseg + kvh * p.nRB + rb;
+    const int ns = sp.seg_info[2 * sigma + 1];
+    const size_t base = (size_t)sp.seg_info[2 * sigma] * sp.rows_block + (rho - rb * sp.rows_block);
+    const int L = p.ctx_lens[b];
+
+    // mask check once per distinct sequence of the wave's rows (the
+    // visibility build needs the whole wave; its verdict is wave-uniform)
+    bool ok = true;
+    int prev_b = -1;
+    bool prev_ok = true;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int bk = __shfl(b, 16 * k);
+      bool okk = prev_ok;
+      if (bk != prev_b) {
+        node_visibility(p.mask_kind[bk], lane_mask_id(p, bk, lane), p.W, p.lookback, lane, okk);
+        prev_b = bk;
+        prev_ok = okk;
+      }
+      if (gq == k) ok = okk;
+    }
+    const bool ctx_ok = L >= 0 && L <= p.max_ctx;
+    float* o = p.out + row * D + gl * VPL;
+    if (!ok || !ctx_ok) {
+      if (live) {
+        if (gl == 0 && w == 0 && h == 0)
+          raise_status((ok ? 0u : MTP_DEV_BAD_MASK) | (ctx_ok ? 0u : MTP_DEV_BAD_CTX));
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) o[j] = qnan();
+        if (p.lse != nullptr && gl == 0) p.lse[row] = qnan();
+      }
+      continue;
+    }
+
+    float M = neg_inf(), den = 0.f;
+    float a[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) a[j] = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+      float ms[4], ls[4];
+      float4 v[4][VPL / 4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sl = s0 + u < ns ? s0 + u : s0;  // in range; dropped below
+        const size_t i = base + (size_t)sl * sp.rows_block;
+        ms[u] = p.part_ml[2 * i];
+        ls[u] = p.part_ml[2 * i + 1];
+        const float4* src = reinterpret_cast<const float4*>(p.part_acc + i * D + gl * VPL);
+#pragma unroll
+        for (int j = 0; j < VPL / 4; ++j) v[u][j] = src[j];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (s0 + u < ns) {
+          const float mn = fmaxf(M, ms[u]);
+          const float mu = mn == neg_inf() ? 0.f : mn;
+          const float cold = fast_exp2(M - mu);
+          const float cnew = fast_exp2(ms[u] - mu);
+          den = den * cold + ls[u] * cnew;
+#pragma unroll
+          for (int j = 0; j < VPL / 4; ++j) {
+            a[4 * j] = a[4 * j] * cold + v[u][j].x * cnew;
+            a[4 * j + 1] = a[4 * j + 1] * cold + v[u][j].y * cnew;
+            a[4 * j + 2] = a[4 * j + 2] * cold + v[u][j].z * cnew;
+            a[4 * j + 3] = a[4 * j + 3] * cold + v[u][j].w * cnew;
+          }
+          M = mn;
+        }
+      }
+    }
+    if (live) {
+      const float inv = 1.f / den;
+      float4* dst = reinterpret_cast<float4*>(o);
+#pragma unroll
+      for (int j = 0; j < VPL / 4; ++j)
+        dst[j] = make_float4(a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv, a[4 * j + 3] * inv);
+      if (p.lse != nullptr && gl == 0) p.lse[row] = (M + log2f(den)) * kLn2;
+    }
+  }
+}
+
 template <int D, bool kStream>
 __global__ __launch_bounds__(256) void attn_combine(AttnParams p, StreamParams sp) {
-  combine_rows<D, kStream>(p, sp, blockIdx.x, blockDim.x >> 6);
+  if constexpr (kStream)
+    combine_rows_stream<D>(p, sp, blockIdx.x, gridDim.x, blockDim.x >> 6);
+  else
+    combine_rows<D>(p, blockIdx.x, blockDim.x >> 6);
 }
 
 // The step's second launch: one acceptance + commit workgroup per sequence
 // (first, so that they are dispatched first: they hold the longest chain of
-// dependent loads), then combine workgroups for every output row.  The two
+// dependent loads), then combine workgroups for every output row
+// (combine_rows_per_block combine waves each).  The two
 // parts touch disjoint data (the commit writes cache slots at or past each
 // context length and ctx_lens_out, which must not alias the ctx_lens the
 // combine reads), so they run side by side.  A combine workgroup takes
@@ -210,8 +289,10 @@ __global__ __launch_bounds__(kAcceptThreads) void finish_kernel(AttnParams p, St
   __shared__ int sm[kAcceptScratchInts];
   if ((int)blockIdx.x < p.B)
     accept_commit_seq(ap, cp, (int)blockIdx.x, sm);
+  else if constexpr (kStream)
+    combine_rows_stream<D>(p, sp, blockIdx.x - p.B, gridDim.x - p.B, combine_rows_per_block);
   else
-    combine_rows<D, kStream>(p, sp, blockIdx.x - p.B, combine_rows_per_block);
+    combine_rows<D>(p, blockIdx.x - p.B, combine_rows_per_block);
 }
 
 }  // namespace mtpv

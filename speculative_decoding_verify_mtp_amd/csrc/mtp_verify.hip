@@ -176,24 +176,33 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
   }
 }
 
-// Workgroups of a combine launch with `rows` output rows (waves) per workgroup.
-unsigned combine_blocks(const AttnParams& p, int rows = 4) {
-  return (unsigned)(((size_t)p.B * p.W * p.Hq + rows - 1) / rows);
+// Output rows one combine wave takes: four (one per 16-lane group) for the
+// stream layout, one for the split layout.
+int combine_rows_per_wave(const Plan& pl) { return pl.kernel == kMfmaStream ? 4 : 1; }
+
+// Workgroups of a combine launch with `waves` combine waves per workgroup.
+// Stream-layout waves loop over their rows, so at most `cap` workgroups.
+unsigned combine_blocks(const AttnParams& p, const Plan& pl, int waves = 4, long cap = 0) {
+  const size_t per = (size_t)waves * combine_rows_per_wave(pl);
+  const long n = (long)(((size_t)p.B * p.W * p.Hq + per - 1) / per);
+  return (unsigned)(pl.kernel == kMfmaStream && cap > 0 ? std::max(1L, std::min(n, cap)) : n);
 }
 
-// Rows per combine workgroup of the step's finish launch.  Its workgroups
+// Combine waves per workgroup of the step's finish launch.  Its workgroups
 // have kAcceptThreads threads, one per compute unit at a time; the rows are
 // spread so that the combine workgroups and the B acceptance workgroups fit
-// on the compute units together, within [4, one row per wave].
-int finish_combine_rows(const AttnParams& p) {
-  const long rows = (long)p.B * p.W * p.Hq;
+// on the compute units together, within [4, all 16 waves] (the stream layout
+// has no lower bound: its waves take four rows each).
+int finish_combine_waves(const AttnParams& p, const Plan& pl) {
+  const int rpw = combine_rows_per_wave(pl);
+  const long waves = ((long)p.B * p.W * p.Hq + rpw - 1) / rpw;
   const long free_cus = std::max(1L, (long)kCUs - p.B);
-  const long per = (rows + free_cus - 1) / free_cus;
-  return (int)std::min<long>(kAcceptThreads / kWave, std::max(4L, per));
+  const long per = (waves + free_cus - 1) / free_cus;
+  return (int)std::min<long>(kAcceptThreads / kWave, std::max(rpw > 1 ? 1L : 4L, per));
 }
 
 void launch_combine(const Attn& a, int D, hipStream_t strm) {
-  const dim3 cgrid(combine_blocks(a.p)), block(256);
+  const dim3 cgrid(combine_blocks(a.p, a.pl, 4, 4L * kCUs)), block(256);
   if (a.pl.kernel == kMfmaStream) attn_combine<128, true><<<cgrid, block, 0, strm>>>(a.p, a.sp);
   else if (D == 128) attn_combine<128, false><<<cgrid, block, 0, strm>>>(a.p, a.sp);
   else attn_combine<64, false><<<cgrid, block, 0, strm>>>(a.p, a.sp);
@@ -385,8 +394,10 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
     launch_combine(a, shape->D, strm);
     accept_commit_kernel<<<dim3(shape->B), dim3(kAcceptThreads), 0, strm>>>(ap, cp);
   } else {
-    const int crows = finish_combine_rows(a.p);
-    const dim3 fgrid((unsigned)shape->B + combine_blocks(a.p, crows)), block(kAcceptThreads);
+    const int crows = finish_combine_waves(a.p, a.pl);
+    const long free_cus = std::max(1L, (long)kCUs - shape->B);
+    const dim3 fgrid((unsigned)shape->B + combine_blocks(a.p, a.pl, crows, free_cus)),
+        block(kAcceptThreads);
     if (a.pl.kernel == kMfmaStream)
       finish_kernel<128, true><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);
     else if (shape->D == 128)
