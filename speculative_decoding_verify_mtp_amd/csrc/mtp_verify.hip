@@ -191,14 +191,14 @@ unsigned combine_blocks(const AttnParams& p, const Plan& pl, int waves = 4, long
 // Combine waves per workgroup of the step's finish launch.  Its workgroups
 // have kAcceptThreads threads, one per compute unit at a time; the rows are
 // spread so that the combine workgroups and the B acceptance workgroups fit
-// on the compute units together, within [4, all 16 waves] (the stream layout
-// has no lower bound: its waves take four rows each).
+// on the compute units together (few rows: one combine wave per workgroup,
+// so that they spread over as many compute units as possible).
 int finish_combine_waves(const AttnParams& p, const Plan& pl) {
   const int rpw = combine_rows_per_wave(pl);
   const long waves = ((long)p.B * p.W * p.Hq + rpw - 1) / rpw;
   const long free_cus = std::max(1L, (long)kCUs - p.B);
   const long per = (waves + free_cus - 1) / free_cus;
-  return (int)std::min<long>(kAcceptThreads / kWave, std::max(rpw > 1 ? 1L : 4L, per));
+  return (int)std::min<long>(kAcceptThreads / kWave, std::max(1L, per));
 }
 
 void launch_combine(const Attn& a, int D, hipStream_t strm) {
