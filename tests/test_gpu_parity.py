@@ -112,6 +112,8 @@ STREAM_HEADS = [
     W_("stream_hkv16", B=10, Hq=32, Hkv=16, W=8, ctx_lo=0, ctx_hi=700, masks="tree"),
     # more KV heads than persistent workgroups: one range per head
     W_("stream_hkv600", B=8, Hq=600, Hkv=600, W=16, ctx_lo=0, ctx_hi=100, masks="chain"),
+    # 33 rows per sequence: the combine's four-row waves straddle sequences
+    W_("stream_rows_straddle", B=9, Hq=3, Hkv=1, W=11, ctx_lo=0, ctx_hi=400, masks="mixed"),
 ]
 
 
@@ -375,8 +377,9 @@ def test_commit_then_attend_equals_verify_rows():
 # data errors: poisoned outputs and the sticky status word, never a fault
 # ----------------------------------------------------------------------------
 
-def test_malformed_mask_poisons_only_that_sequence():
-    wl = W_("bad_mask", B=3, Hq=8, Hkv=2, W=8, ctx_lo=30, ctx_hi=90, masks="tree")
+@pytest.mark.parametrize("B", [3, 9], ids=["split", "stream"])
+def test_malformed_mask_poisons_only_that_sequence(B):
+    wl = W_("bad_mask", B=B, Hq=8, Hkv=2, W=8, ctx_lo=30, ctx_hi=90, masks="tree")
     inp = gpu_inputs(wl, 2)
     lib.device_status(clear=True)
     ids = inp["mask_ids"].clone()
@@ -385,8 +388,9 @@ def test_malformed_mask_poisons_only_that_sequence():
     out, lse = run_attn(inp)
     assert torch.isnan(out[1]).all() and torch.isnan(lse[1]).all()
     ref_out, ref_lse = oracle_attn(inp)
-    keep = torch.tensor([0, 2], device=out.device)
-    assert_attn_close(out[keep], lse[keep], ref_out[[0, 2]], ref_lse[[0, 2]], *tol_for(wl))
+    rest = [b for b in range(B) if b != 1]
+    keep = torch.tensor(rest, device=out.device)
+    assert_attn_close(out[keep], lse[keep], ref_out[rest], ref_lse[rest], *tol_for(wl))
     n, path, bonus = lib.accept(inp["logits"], inp["draft_ids"], inp["mask_kind"], ids)
     assert_accept_equal((n, path, bonus), oracle_accept(inp))
     assert lib.device_status(clear=True) & lib.DEV_BAD_MASK
@@ -398,6 +402,25 @@ def test_context_above_bound_poisons_that_sequence():
     lib.device_status(clear=True)
     out, lse = run_attn(inp, max_ctx_len=39)
     assert torch.isnan(out).all() and torch.isnan(lse).all()
+    assert lib.device_status(clear=True) & lib.DEV_BAD_CTX
+
+
+def test_stream_context_above_bound_poisons_only_that_sequence():
+    """Stream schedule: sequences past max_ctx_len get no stages and NaN rows;
+    the others are unaffected."""
+    wl = W_("bad_ctx_stream", B=9, Hq=8, Hkv=2, W=8, ctx_lo=20, ctx_hi=300, masks="mixed")
+    inp = gpu_inputs(wl, 3)
+    ctx = [int(x) for x in inp["host"]["ctx_lens"]]
+    bound = max(ctx) - 1
+    lib.device_status(clear=True)
+    out, lse = run_attn(inp, max_ctx_len=bound)
+    bad = [b for b in range(wl.B) if ctx[b] > bound]
+    rest = [b for b in range(wl.B) if ctx[b] <= bound]
+    assert bad and rest
+    assert torch.isnan(out[bad]).all() and torch.isnan(lse[bad]).all()
+    ref_out, ref_lse = oracle_attn(inp)
+    keep = torch.tensor(rest, device=out.device)
+    assert_attn_close(out[keep], lse[keep], ref_out[rest], ref_lse[rest], *tol_for(wl))
     assert lib.device_status(clear=True) & lib.DEV_BAD_CTX
 
 
@@ -451,6 +474,7 @@ def test_empty_batch_is_a_no_op():
 
 STEP = [
     W_("step_mixed_b9", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=700, masks="mixed"),
+    W_("step_stream_straddle", B=9, Hq=3, Hkv=1, W=11, ctx_lo=10, ctx_hi=400, masks="mixed"),
     W_("step_chain_b1", B=1, Hq=20, Hkv=5, W=8, ctx_lo=600, ctx_hi=600),
     W_("step_segment_d64", B=3, Hq=16, Hkv=16, D=64, W=16, ctx_lo=30, ctx_hi=300,
        masks="segment", seg_lookback=1),
