@@ -255,11 +255,15 @@ __device__ __forceinline__ void combine_rows_stream(const AttnParams& p, const S
       }
     }
     if (live) {
+      // Streaming stores: the output is not read again in this step, and
+      // kept out of L2 it does not have to be written back at the launch
+      // boundary (the ragged batch's step is ~8 us shorter).
       const float inv = 1.f / den;
-      float4* dst = reinterpret_cast<float4*>(o);
+      f32x4* dst = reinterpret_cast<f32x4*>(o);
 #pragma unroll
       for (int j = 0; j < VPL / 4; ++j)
-        dst[j] = make_float4(a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv, a[4 * j + 3] * inv);
+        __builtin_nontemporal_store(
+            f32x4{a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv, a[4 * j + 3] * inv}, dst + j);
       if (p.lse != nullptr && gl == 0) p.lse[row] = (M + log2f(den)) * kLn2;
     }
   }
