@@ -403,6 +403,11 @@ void attn_partial_lds(AttnParams p) {
     return;
   }
 
+  // One key slice: the waves lay their rows out row-major in the ring (as
+  // the key-slice path does) and then store whole rows, 1 KB per store
+  // instruction.
+  constexpr int kPitch = D + 4;
+  static_assert(NR * RB * 16 * kPitch * 4 <= kLdsStages * kStageBytes, "row image fits the ring");
   if (bad) {
     if (threadIdx.x == 0) raise_status(MTP_DEV_BAD_PAGE);
 #pragma unroll
@@ -412,33 +417,35 @@ void attn_partial_lds(AttnParams p) {
       for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{qnan(), qnan(), qnan(), qnan()};
     }
   }
-
+  const size_t item_row = (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R;
+  wait_vmem_barrier<0>();  // every wave is done with the ring
+  float* sbuf = reinterpret_cast<float*>(ring);
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
-    float l = st.l[k];
-    l = rows4_sum(l);
+    const float l = rows4_sum(st.l[k]);
     const int rho = (row_tile0 + k) * 16 + c;
-    if (rho < p.R) {
-      const size_t pidx =
-          (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R + rho;
-      if (qd == 0) {
-        p.part_ml[2 * pidx] = st.m[k];
-        p.part_ml[2 * pidx + 1] = l;
-      }
-      float* dst = p.part_acc + pidx * D + qd * (D / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int t = 0; t < NT; t += 4) {
-          float4 v;
-          v.x = st.acc[k][t][e];
-          v.y = st.acc[k][t + 1][e];
-          v.z = st.acc[k][t + 2][e];
-          v.w = st.acc[k][t + 3][e];
-          *reinterpret_cast<float4*>(dst + e * (D / 16) + t) = v;
-        }
-      }
+    if (qd == 0 && rho < p.R) {
+      p.part_ml[2 * (item_row + rho)] = st.m[k];
+      p.part_ml[2 * (item_row + rho) + 1] = l;
     }
+    float* rowp = sbuf + (size_t)((tg * RB + k) * 16 + c) * kPitch + qd * (D / 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int t = 0; t < NT; t += 4)
+        *reinterpret_cast<float4*>(rowp + e * (D / 16) + t) =
+            make_float4(st.acc[k][t][e], st.acc[k][t + 1][e], st.acc[k][t + 2][e], st.acc[k][t + 3][e]);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int row0 = it.rb * NR * RB * 16;  // first row of this workgroup's row block
+  constexpr int kVecs = NR * RB * 16 * (D / 4);
+#pragma unroll 4
+  for (int f = threadIdx.x; f < kVecs; f += 64 * NW) {
+    const int row = f / (D / 4);
+    const int col = f - row * (D / 4);
+    if (row0 + row < p.R)
+      *reinterpret_cast<float4*>(p.part_acc + (item_row + row0 + row) * D + col * 4) =
+          *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4);
   }
 }
 
