@@ -312,29 +312,65 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
         }
       }
       const size_t piece = (size_t)piece0 + lsig;
+      constexpr int kPitch = D + 4;  // padded rows: the 16 rows a write spans fall in different banks
+      if constexpr (NR * RB * 16 * kPitch * 4 <= NS * kStageBytes) {
+        // The ring is idle (the run has drained it): the waves lay the
+        // piece's rows out row-major there, then store whole rows, 1 KB per
+        // store instruction.
+        float* sbuf = reinterpret_cast<float*>(ring);
 #pragma unroll
-      for (int k = 0; k < RB; ++k) {
-        float l = st.l[k];
-        l = rows4_sum(l);
-        const int rl = (wv * RB + k) * 16 + c;  // row within the block
-        const int rho = rb * sp.rows_block + rl;
-        if (rho < p.R) {
-          const size_t pidx = piece * sp.rows_block + rl;
-          if (qd == 0) {
+        for (int k = 0; k < RB; ++k) {
+          const float l = rows4_sum(st.l[k]);
+          const int rl = (wv * RB + k) * 16 + c;  // row within the block
+          if (qd == 0 && rb * sp.rows_block + rl < p.R) {
+            const size_t pidx = piece * sp.rows_block + rl;
             p.part_ml[2 * pidx] = st.m[k];
             p.part_ml[2 * pidx + 1] = l;
           }
-          float* dst = p.part_acc + pidx * D + qd * (D / 4);
+          float* rowp = sbuf + (size_t)rl * kPitch + qd * (D / 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int t = 0; t < NT; t += 4) {
-              float4 v;
-              v.x = st.acc[k][t][e];
-              v.y = st.acc[k][t + 1][e];
-              v.z = st.acc[k][t + 2][e];
-              v.w = st.acc[k][t + 3][e];
-              *reinterpret_cast<float4*>(dst + e * (D / 16) + t) = v;
+            for (int t = 0; t < NT; t += 4)
+              *reinterpret_cast<float4*>(rowp + e * (D / 16) + t) =
+                  make_float4(st.acc[k][t][e], st.acc[k][t + 1][e], st.acc[k][t + 2][e], st.acc[k][t + 3][e]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int nvec = sp.rows_block * (D / 4);
+        for (int f = threadIdx.x; f < nvec; f += 64 * NR) {
+          const int row = f / (D / 4);
+          const int col = f - row * (D / 4);
+          if (rb * sp.rows_block + row < p.R)
+            *reinterpret_cast<float4*>(p.part_acc + (piece * sp.rows_block + row) * D + col * 4) =
+                *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4);
+        }
+        // the next run refills the ring: every wave is done reading the rows
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      } else {
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+          float l = st.l[k];
+          l = rows4_sum(l);
+          const int rl = (wv * RB + k) * 16 + c;  // row within the block
+          const int rho = rb * sp.rows_block + rl;
+          if (rho < p.R) {
+            const size_t pidx = piece * sp.rows_block + rl;
+            if (qd == 0) {
+              p.part_ml[2 * pidx] = st.m[k];
+              p.part_ml[2 * pidx + 1] = l;
+            }
+            float* dst = p.part_acc + pidx * D + qd * (D / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+#pragma unroll
+              for (int t = 0; t < NT; t += 4) {
+                float4 v;
+                v.x = st.acc[k][t][e];
+                v.y = st.acc[k][t + 1][e];
+                v.z = st.acc[k][t + 2][e];
+                v.w = st.acc[k][t + 3][e];
+                *reinterpret_cast<float4*>(dst + e * (D / 16) + t) = v;
+              }
             }
           }
         }
