@@ -439,29 +439,64 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
     }
   }
 
+  const size_t item_row = (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R;
+  constexpr int kPitch = D + 4;  // padded rows: the 16 rows a write spans fall in different banks
+  if constexpr (NR * RB * 16 * kPitch * 4 <= kNestRingStages * kNestCodeBytes) {
+    // Rows staged row-major in the code ring, then stored as whole rows (1 KB
+    // per store instruction) by every wave.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // nobody reads the ring any more
+    float* sbuf = reinterpret_cast<float*>(ring);
 #pragma unroll
-  for (int k = 0; k < RB; ++k) {
-    float l = st.l[k];
-    l = rows4_sum(l);
-    const int rho = (row_tile0 + k) * 16 + c;
-    if (rho < p.R) {
-      const size_t pidx =
-          (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R + rho;
-      if (qd == 0) {
-        p.part_ml[2 * pidx] = st.m[k];
-        p.part_ml[2 * pidx + 1] = l;
+    for (int k = 0; k < RB; ++k) {
+      const float l = rows4_sum(st.l[k]);
+      const int rho = (row_tile0 + k) * 16 + c;
+      if (qd == 0 && rho < p.R) {
+        p.part_ml[2 * (item_row + rho)] = st.m[k];
+        p.part_ml[2 * (item_row + rho) + 1] = l;
       }
-      float* dst = p.part_acc + pidx * D + qd * (D / 4);
+      float* rowp = sbuf + (size_t)((wv * RB + k) * 16 + c) * kPitch + qd * (D / 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int t = 0; t < NT; t += 4) {
-          float4 v;
-          v.x = st.acc[k][t][e];
-          v.y = st.acc[k][t + 1][e];
-          v.z = st.acc[k][t + 2][e];
-          v.w = st.acc[k][t + 3][e];
-          *reinterpret_cast<float4*>(dst + e * (D / 16) + t) = v;
+        for (int t = 0; t < NT; t += 4)
+          *reinterpret_cast<float4*>(rowp + e * (D / 16) + t) =
+              make_float4(st.acc[k][t][e], st.acc[k][t + 1][e], st.acc[k][t + 2][e], st.acc[k][t + 3][e]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int row0 = it.rb * NR * RB * 16;  // first row of this workgroup's row block
+    constexpr int kVecs = NR * RB * 16 * (D / 4);
+#pragma unroll 4
+    for (int f = threadIdx.x; f < kVecs; f += 64 * NR) {
+      const int row = f / (D / 4);
+      const int col = f - row * (D / 4);
+      if (row0 + row < p.R)
+        *reinterpret_cast<float4*>(p.part_acc + (item_row + row0 + row) * D + col * 4) =
+            *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      float l = st.l[k];
+      l = rows4_sum(l);
+      const int rho = (row_tile0 + k) * 16 + c;
+      if (rho < p.R) {
+        const size_t pidx = item_row + rho;
+        if (qd == 0) {
+          p.part_ml[2 * pidx] = st.m[k];
+          p.part_ml[2 * pidx + 1] = l;
+        }
+        float* dst = p.part_acc + pidx * D + qd * (D / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int t = 0; t < NT; t += 4) {
+            float4 v;
+            v.x = st.acc[k][t][e];
+            v.y = st.acc[k][t + 1][e];
+            v.z = st.acc[k][t + 2][e];
+            v.w = st.acc[k][t + 3][e];
+            *reinterpret_cast<float4*>(dst + e * (D / 16) + t) = v;
+          }
         }
       }
     }
