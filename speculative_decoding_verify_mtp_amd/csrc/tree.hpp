@@ -55,12 +55,14 @@ constexpr int kTreeMaxV = kTreeListThreads * kTreeListElems;
 // passes over 8-bit digits, most significant first, find the k-th largest
 // key (k = min(n, V)): each pass histograms the digit of the keys that match
 // the digits found so far (LDS atomics) and wave 0 walks the bins from the
-// top.  The k keys at or above it are then appended to LDS and put in order
-// by counting, for each, the keys above it.
+// top.  The passes stop early once the selected bin holds exactly the keys
+// still to be taken (the lower digits then change nothing: every key with
+// the prefix is among the k).  The k keys at or above the prefix are then
+// appended to LDS and put in order by counting, for each, the keys above it.
 __global__ __launch_bounds__(kTreeListThreads) void tree_lists_kernel(TreeParams p) {
   __shared__ int s_hist[256];
   __shared__ unsigned long long s_prefix;
-  __shared__ int s_k, s_cnt;
+  __shared__ int s_k, s_cnt, s_cbin;
   __shared__ unsigned long long s_key[kTreeMaxList];
   const int d = blockIdx.x;
   const int b = blockIdx.y;
@@ -110,6 +112,7 @@ __global__ __launch_bounds__(kTreeListThreads) void tree_lists_kernel(TreeParams
           if (acc < k && k <= acc + c[u]) {
             s_prefix = prefix | ((unsigned long long)(255 - 4 * lane - u) << sh);
             s_k = k - acc;
+            s_cbin = c[u];
           }
           acc += c[u];
         }
@@ -118,6 +121,7 @@ __global__ __launch_bounds__(kTreeListThreads) void tree_lists_kernel(TreeParams
     __syncthreads();
     prefix = s_prefix;
     k = s_k;
+    if (k == s_cbin) break;  // the whole bin is taken (uniform: read from LDS)
   }
   // the kk keys at or above the kk-th largest
   if (tid == 0) s_cnt = 0;
