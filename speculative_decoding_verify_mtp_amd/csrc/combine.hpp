@@ -9,7 +9,7 @@
 // four groups of sixteen lanes: group q takes splits q, q+4, ..., each lane
 // D/16 consecutive accumulators, so every load is 16-byte wide and many are
 // in flight; the four group sums are folded with two shuffles.
-// Stream layout (combine_rows_stream): four rows per wave, see there.
+// Few partials per row (combine_rows_grouped): four rows per wave, see there.
 #pragma once
 
 #include "accept_commit.hpp"
@@ -153,16 +153,17 @@ __device__ __forceinline__ void combine_rows(const AttnParams& p, unsigned block
   if (p.lse != nullptr && lane == 0) p.lse[row] = (M + log2f(den)) * kLn2;
 }
 
-// Stream layout: a row has few pieces (a segment spans one to a few
-// ranges), so one row per wave would leave most lanes idle and the rows would
-// take many rounds of waves, each paying the two dependent round trips
-// (segment table, then pieces).  Here each 16-lane group of a wave takes its
-// own row (rows 4 r .. 4 r + 3 of the flat [B, W, Hq] order), each lane D/16
-// consecutive columns, and folds the row's pieces online, four pieces' loads
-// in flight at a time.  Pieces past the row's count are dropped by selection.
-template <int D>
-__device__ __forceinline__ void combine_rows_stream(const AttnParams& p, const StreamParams& sp,
-                                                    unsigned block, unsigned nblocks, int waves) {
+// Rows with few partials (the stream layout, where a segment spans one to a
+// few ranges; the split layout with at most kGroupedMaxSplits splits): one
+// row per wave would leave most lanes idle and the rows would take many
+// rounds of waves, each paying its dependent round trips.  Here each 16-lane
+// group of a wave takes its own row (rows 4 r .. 4 r + 3 of the flat
+// [B, W, Hq] order), each lane D/16 consecutive columns, and folds the row's
+// partials online, four partials' loads in flight at a time.  Partials past
+// the row's count are dropped by selection.
+template <int D, bool kStream>
+__device__ __forceinline__ void combine_rows_grouped(const AttnParams& p, const StreamParams& sp,
+                                                     unsigned block, unsigned nblocks, int waves) {
   constexpr int VPL = D / 16;  // columns per lane
   const int lane = threadIdx.x & 63;
   const int gq = lane >> 4, gl = lane & 15;
@@ -183,10 +184,19 @@ __device__ __forceinline__ void combine_rows_stream(const AttnParams& p, const S
     const int b = (int)(bw / p.W);
     const int kvh = h / p.g;
     const int rho = w * p.g + (h - kvh * p.g);
-    const int rb = rho / sp.rows_block;
-    const int sigma = b * sp.nseg + kvh * p.nRB + rb;
-    const int ns = sp.seg_info[2 * sigma + 1];
-    const size_t base = (size_t)sp.seg_info[2 * sigma] * sp.rows_block + (rho - rb * sp.rows_block);
+    int ns;                // partials of the row (split layout: known once L is)
+    size_t base, stride;   // row of partial s: base + s * stride
+    if constexpr (kStream) {
+      const int rb = rho / sp.rows_block;
+      const int sigma = b * sp.nseg + kvh * p.nRB + rb;
+      ns = sp.seg_info[2 * sigma + 1];
+      base = (size_t)sp.seg_info[2 * sigma] * sp.rows_block + (rho - rb * sp.rows_block);
+      stride = (size_t)sp.rows_block;
+    } else {
+      ns = 0;
+      base = (((size_t)b * p.max_splits) * p.Hkv + kvh) * (size_t)p.R + rho;
+      stride = (size_t)p.Hkv * p.R;
+    }
     const int L = p.ctx_lens[b];
 
     // mask check once per distinct sequence of the wave's rows (the
@@ -218,6 +228,7 @@ __device__ __forceinline__ void combine_rows_stream(const AttnParams& p, const S
       continue;
     }
 
+    if constexpr (!kStream) ns = num_splits(L, p.S);
     float M = neg_inf(), den = 0.f;
     float a[VPL];
 #pragma unroll
@@ -228,7 +239,7 @@ __device__ __forceinline__ void combine_rows_stream(const AttnParams& p, const S
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int sl = s0 + u < ns ? s0 + u : s0;  // in range; dropped below
-        const size_t i = base + (size_t)sl * sp.rows_block;
+        const size_t i = base + (size_t)sl * stride;
         ms[u] = p.part_ml[2 * i];
         ls[u] = p.part_ml[2 * i + 1];
         const float4* src = reinterpret_cast<const float4*>(p.part_acc + i * D + gl * VPL);
@@ -272,7 +283,9 @@ __device__ __forceinline__ void combine_rows_stream(const AttnParams& p, const S
 template <int D, bool kStream>
 __global__ __launch_bounds__(256) void attn_combine(AttnParams p, StreamParams sp) {
   if constexpr (kStream)
-    combine_rows_stream<D>(p, sp, blockIdx.x, gridDim.x, blockDim.x >> 6);
+    combine_rows_grouped<D, true>(p, sp, blockIdx.x, gridDim.x, blockDim.x >> 6);
+  else if (grouped_split_combine(p.max_splits, (long)p.B * p.W * p.Hq))
+    combine_rows_grouped<D, false>(p, sp, blockIdx.x, gridDim.x, blockDim.x >> 6);
   else
     combine_rows<D>(p, blockIdx.x, blockDim.x >> 6);
 }
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(kAcceptThreads) void finish_kernel(AttnParams p, St
   if ((int)blockIdx.x < p.B)
     accept_commit_seq(ap, cp, (int)blockIdx.x, sm);
   else if constexpr (kStream)
-    combine_rows_stream<D>(p, sp, blockIdx.x - p.B, gridDim.x - p.B, combine_rows_per_block);
+    combine_rows_grouped<D, true>(p, sp, blockIdx.x - p.B, gridDim.x - p.B, combine_rows_per_block);
   else
     combine_rows<D>(p, blockIdx.x - p.B, combine_rows_per_block);
 }

@@ -25,6 +25,18 @@ __device__ __forceinline__ void raise_status(unsigned bits) { atomicOr(&g_status
 // Splits of an output row whose accumulators the combine requests in its
 // first batch (four 16-lane groups of kCombineFast / 4).
 constexpr int kCombineFast = 32;
+// In a combine launch of its own, split-layout rows with at most
+// kGroupedMaxSplits splits are combined four rows per wave (one per 16-lane
+// group), like the stream layout's, when there are enough rows for the waves
+// to take several rounds (with few rows, one row per wave has all of a row's
+// splits in flight at once).  The step's finish launch keeps one row per wave
+// for the split layout (a larger finish kernel cost the latency-bound steps
+// more than it saved).
+constexpr int kGroupedMaxSplits = 16;
+constexpr long kGroupedMinRows = 4096;
+__host__ __device__ inline bool grouped_split_combine(int max_splits, long rows) {
+  return max_splits <= kGroupedMaxSplits && rows >= kGroupedMinRows;
+}
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float qnan() { return __builtin_nanf(""); }

@@ -177,15 +177,22 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
 }
 
 // Output rows one combine wave takes: four (one per 16-lane group) for the
-// stream layout, one for the split layout.
-int combine_rows_per_wave(const Plan& pl) { return pl.kernel == kMfmaStream ? 4 : 1; }
+// stream layout and for split layouts with few splits, one otherwise.
+// `finish`: the step's finish launch (grouped for the stream layout only).
+bool grouped_combine(const AttnParams& p, const Plan& pl, bool finish) {
+  return pl.kernel == kMfmaStream ||
+         (!finish && grouped_split_combine(pl.max_splits, (long)p.B * p.W * p.Hq));
+}
+int combine_rows_per_wave(const AttnParams& p, const Plan& pl, bool finish) {
+  return grouped_combine(p, pl, finish) ? 4 : 1;
+}
 
 // Workgroups of a combine launch with `waves` combine waves per workgroup.
-// Stream-layout waves loop over their rows, so at most `cap` workgroups.
-unsigned combine_blocks(const AttnParams& p, const Plan& pl, int waves = 4, long cap = 0) {
-  const size_t per = (size_t)waves * combine_rows_per_wave(pl);
+// Grouped-combine waves loop over their rows, so at most `cap` workgroups.
+unsigned combine_blocks(const AttnParams& p, const Plan& pl, bool finish, int waves, long cap) {
+  const size_t per = (size_t)waves * combine_rows_per_wave(p, pl, finish);
   const long n = (long)(((size_t)p.B * p.W * p.Hq + per - 1) / per);
-  return (unsigned)(pl.kernel == kMfmaStream && cap > 0 ? std::max(1L, std::min(n, cap)) : n);
+  return (unsigned)(grouped_combine(p, pl, finish) ? std::max(1L, std::min(n, cap)) : n);
 }
 
 // Combine waves per workgroup of the step's finish launch.  Its workgroups
@@ -194,7 +201,7 @@ unsigned combine_blocks(const AttnParams& p, const Plan& pl, int waves = 4, long
 // on the compute units together (few rows: one combine wave per workgroup,
 // so that they spread over as many compute units as possible).
 int finish_combine_waves(const AttnParams& p, const Plan& pl) {
-  const int rpw = combine_rows_per_wave(pl);
+  const int rpw = combine_rows_per_wave(p, pl, true);
   const long waves = ((long)p.B * p.W * p.Hq + rpw - 1) / rpw;
   const long free_cus = std::max(1L, (long)kCUs - p.B);
   const long per = (waves + free_cus - 1) / free_cus;
@@ -202,7 +209,7 @@ int finish_combine_waves(const AttnParams& p, const Plan& pl) {
 }
 
 void launch_combine(const Attn& a, int D, hipStream_t strm) {
-  const dim3 cgrid(combine_blocks(a.p, a.pl, 4, 4L * kCUs)), block(256);
+  const dim3 cgrid(combine_blocks(a.p, a.pl, false, 4, 4L * kCUs)), block(256);
   if (a.pl.kernel == kMfmaStream) attn_combine<128, true><<<cgrid, block, 0, strm>>>(a.p, a.sp);
   else if (D == 128) attn_combine<128, false><<<cgrid, block, 0, strm>>>(a.p, a.sp);
   else attn_combine<64, false><<<cgrid, block, 0, strm>>>(a.p, a.sp);
@@ -396,7 +403,7 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
   } else {
     const int crows = finish_combine_waves(a.p, a.pl);
     const long free_cus = std::max(1L, (long)kCUs - shape->B);
-    const dim3 fgrid((unsigned)shape->B + combine_blocks(a.p, a.pl, crows, free_cus)),
+    const dim3 fgrid((unsigned)shape->B + combine_blocks(a.p, a.pl, true, crows, free_cus)),
         block(kAcceptThreads);
     if (a.pl.kernel == kMfmaStream)
       finish_kernel<128, true><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);

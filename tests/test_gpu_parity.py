@@ -52,6 +52,10 @@ SMALL = [
     W_("ctx0", B=3, Hq=8, Hkv=8, W=16, ctx_lo=0, ctx_hi=0, masks="mixed"),
     W_("ctx_page_edges", B=4, Hq=8, Hkv=1, W=4, ctx_lo=15, ctx_hi=17),
     W_("mask_tokens", Hq=16, Hkv=4, W=12, ctx_lo=64, ctx_hi=64, mask_token_rows=4),
+    # 4096 output rows with few splits: the combine takes four rows per wave
+    W_("grouped_d64", B=4, Hq=64, Hkv=16, D=64, W=16, ctx_lo=50, ctx_hi=700, masks="mixed"),
+    W_("grouped_fp32", B=2, Hq=64, Hkv=64, D=64, W=32, dtype="f32", ctx_lo=20, ctx_hi=300,
+       masks="tree"),
 ]
 
 
@@ -475,6 +479,7 @@ def test_empty_batch_is_a_no_op():
 STEP = [
     W_("step_mixed_b9", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=700, masks="mixed"),
     W_("step_stream_straddle", B=9, Hq=3, Hkv=1, W=11, ctx_lo=10, ctx_hi=400, masks="mixed"),
+    W_("step_grouped_b4", B=4, Hq=64, Hkv=8, W=16, ctx_lo=50, ctx_hi=600, masks="mixed"),
     W_("step_chain_b1", B=1, Hq=20, Hkv=5, W=8, ctx_lo=600, ctx_hi=600),
     W_("step_segment_d64", B=3, Hq=16, Hkv=16, D=64, W=16, ctx_lo=30, ctx_hi=300,
        masks="segment", seg_lookback=1),
