@@ -132,6 +132,34 @@ def test_stream_ranges_per_kv_head(wl, split):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"{wl.name} split {split}")
 
 
+PHASES = [
+    W_("phase_split", B=3, Hq=20, Hkv=5, W=8, ctx_lo=100, ctx_hi=900),
+    W_("phase_stream", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=900, masks="mixed"),
+    W_("phase_grouped", B=4, Hq=64, Hkv=16, D=64, W=16, ctx_lo=50, ctx_hi=700, masks="mixed"),
+]
+
+
+@pytest.mark.parametrize("wl", PHASES, ids=[w.name for w in PHASES])
+def test_partial_then_combine_equals_the_fused_call(wl):
+    """mtp_verify_attn_partial then mtp_verify_attn_combine on one workspace
+    give exactly what mtp_verify_attn gives (the same kernels in order)."""
+    inp = gpu_inputs(wl, 23)
+    mc = int(inp["host"]["ctx_lens"].max())
+    args = (inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["ctx_lens"],
+            inp["k_new"], inp["v_new"], inp["mask_kind"], inp["mask_ids"])
+    kw = dict(max_ctx_len=mc, scale=inp["scale"], seg_lookback=inp["seg_lookback"])
+    out, lse = lib.verify_attn(*args, **kw)
+    ws = torch.empty(max(lib.workspace_bytes(lib.shape_of(inp["q"], inp["k_cache"],
+                                                          inp["block_table"], **kw)), 16),
+                     dtype=torch.uint8, device=out.device)
+    o2 = torch.full_like(out, float("nan"))
+    l2 = torch.full_like(lse, float("nan"))
+    lib.verify_attn(*args, out=o2, lse=l2, workspace=ws, phase="partial", **kw)
+    lib.verify_attn(*args, out=o2, lse=l2, workspace=ws, phase="combine", **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
 def test_loose_max_ctx_len_bound():
     """max_ctx_len only sizes the split plan; a loose bound gives the same result."""
     wl = W_("loose", B=2, Hq=8, Hkv=2, W=8, ctx_lo=10, ctx_hi=300, masks="tree")
