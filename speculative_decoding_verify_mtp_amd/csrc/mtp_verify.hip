@@ -156,7 +156,6 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
     const dim3 wblock(64 * pl.NR * pl.KS);
     if (pl.KS == 2 && pl.NR == 2) attn_partial_lds<1, 2, 2><<<wgrid, wblock, 0, strm>>>(p);
     else if (pl.KS == 2) attn_partial_lds<1, 1, 2><<<wgrid, wblock, 0, strm>>>(p);
-    else if (pl.RB == 2) attn_partial_lds<2, 4><<<wgrid, wblock, 0, strm>>>(p);
     else if (pl.NR == 4) attn_partial_lds<1, 4><<<wgrid, wblock, 0, strm>>>(p);
     else if (pl.NR == 2) attn_partial_lds<1, 2><<<wgrid, wblock, 0, strm>>>(p);
     else attn_partial_lds<1, 1><<<wgrid, wblock, 0, strm>>>(p);

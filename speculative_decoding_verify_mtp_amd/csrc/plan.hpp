@@ -43,7 +43,7 @@ struct Plan {
   Kernel kernel;   // VALU (fp32, or < 16 rows), MFMA with direct loads (D=64), MFMA + LDS ring (D=128)
   bool mfma;       // bf16 with >= 16 rows per KV head
   int g, R;        // group size, rows per KV head (W * g)
-  int RB;          // MFMA row tiles per wave (1, 2 or 4)
+  int RB;          // MFMA row tiles per wave (1, 2 or 4; the per-split LDS kernel runs 1)
   int NR;          // row-tile groups (waves) per workgroup (LDS kernel; 1 wave per item otherwise)
   int KS;          // key slices per workgroup (LDS kernel: NR * KS waves)
   int nRB;         // row blocks (MFMA) or row chunks (VALU) per KV head
@@ -163,6 +163,19 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
       pl.G = (int)((Gh < 1 ? 1 : (Gh > max_h ? max_h : Gh)) * s.Hkv);
       rows = ((size_t)pl.G + (size_t)s.B * pl.nseg) * pl.rows_block;
     }
+  }
+  // Per-split LDS kernel with two row tiles per wave (more than 64 rows per
+  // KV head): the split stays sized for 128-row workgroups, but each is run
+  // as two workgroups of one row tile per wave.  Two row tiles per wave need
+  // all 512 registers of a SIMD lane, so a compute unit holds one such
+  // workgroup (one wave per SIMD, nothing to overlap a wave's stage chain
+  // with); one tile per wave leaves room for two workgroups per CU.  The two
+  // row blocks of a (split, head) read the same K/V; the kernel places them
+  // eight workgroups apart, on the same XCD, so the second read is served
+  // by that XCD's L2 (llama3_8b_tree partial 23.2 -> 20.6 us).
+  if (pl.kernel == kMfmaLds && pl.RB == 2) {
+    pl.RB = 1;
+    pl.nRB = (tiles + pl.NR - 1) / pl.NR;
   }
   pl.acc_bytes = rows * s.D * sizeof(float);
   pl.ml_offset = (pl.acc_bytes + 255) & ~(size_t)255;

@@ -114,7 +114,9 @@ def test_empty_batch_needs_no_pointers(L):
 
 def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     """The documented split plan: rows per KV head R = W * g; bf16 with R >= 16
-    runs on MFMA (D=128: workgroups of up to 4 waves x 2 row tiles; D=64: one
+    runs on MFMA (D=128: splits sized for workgroups of up to 4 waves x 2 row
+    tiles, which the per-split kernel runs as row blocks of one tile per wave;
+    the workspace does not depend on that; D=64: one
     wave of 1, 2 or 4 row tiles per row block), everything else in chunks of
     4 rows; the automatic split is the power of two giving about 1024
     workgroups (LDS kernel) or 2048 waves (the others), at least twice the

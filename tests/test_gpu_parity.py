@@ -49,6 +49,9 @@ SMALL = [
     W_("w64_tree", Hq=4, Hkv=2, W=64, ctx_lo=90, ctx_hi=400, masks="tree", tree_depth=63),
     W_("w64_chain_d64", Hq=2, Hkv=2, D=64, W=64, ctx_lo=1, ctx_hi=130),
     W_("w33_mixed_g8", B=3, Hq=64, Hkv=8, W=33, ctx_lo=31, ctx_hi=97, masks="mixed"),
+    # 192 rows per KV head: three row blocks per (split, head), 18 such units,
+    # so both the XCD-paired groups of eight units and the tail are used
+    W_("row_blocks3_hkv3", B=3, Hq=36, Hkv=3, W=16, ctx_lo=100, ctx_hi=1500, masks="mixed"),
     W_("ctx0", B=3, Hq=8, Hkv=8, W=16, ctx_lo=0, ctx_hi=0, masks="mixed"),
     W_("ctx_page_edges", B=4, Hq=8, Hkv=1, W=4, ctx_lo=15, ctx_hi=17),
     W_("mask_tokens", Hq=16, Hkv=4, W=12, ctx_lo=64, ctx_hi=64, mask_token_rows=4),
