@@ -101,34 +101,6 @@ __device__ __forceinline__ void wait_stage_barrier(int n) {
 // accumulators, the reference max and the lane's share of the row sum.
 constexpr int kSliceStateFloats = 34;
 
-// Work item of workgroup `item` out of `n_items` = nRB * (splits x heads).
-// Workgroups are dealt to the eight XCDs round robin, and the nRB row blocks
-// of one (split, head) read the same K/V: each group of 8 * nRB consecutive
-// workgroups holds eight (split, head) units, row block r of unit u at
-// position 8 r + u, so a unit's row blocks land on one XCD and share its L2.
-// The last units (fewer than eight) take consecutive positions.
-__device__ __forceinline__ Item decode_item_xcd(int item, int n_items, const AttnParams& p) {
-  const int nrb = p.nRB;
-  const int units = n_items / nrb;
-  const int full = (units / 8) * 8 * nrb;  // workgroups in whole groups
-  int u, rb;
-  if (item < full) {
-    const int grp = item / (8 * nrb);
-    const int r = item - grp * 8 * nrb;
-    rb = r >> 3;
-    u = grp * 8 + (r & 7);
-  } else {
-    const int t = item - full;
-    rb = t % nrb;
-    u = full / nrb + t / nrb;
-  }
-  Item it;
-  it.rb = rb;
-  it.kvh = u % p.Hkv;
-  it.split = u / p.Hkv;
-  return it;
-}
-
 // RB = 1 kernels are held to 256 registers so that two waves share a SIMD.
 // KS > 1 (key slices): the workgroup has NR * KS waves; wave (g, k) owns the
 // row tiles of group g and the stages k, k + KS, ... of the item, and the KS

@@ -155,7 +155,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
   const int c = lane & 15;
   const int qd = lane >> 4;
   const int b = blockIdx.y;
-  const Item it = decode_item(blockIdx.x, p);
+  const Item it = decode_item_xcd(blockIdx.x, gridDim.x, p);
   if (it.split >= p.max_splits) return;  // uniform over the workgroup
   const int start = it.split * p.S;
 

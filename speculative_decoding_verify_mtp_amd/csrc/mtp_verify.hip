@@ -140,8 +140,7 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
   if (pl.kernel == kMfmaNested) {
     const dim3 wgrid((unsigned)items, (unsigned)B);
     const dim3 wblock(64 * pl.NR);
-    if (pl.RB == 2) attn_partial_nested_lds<2, 4><<<wgrid, wblock, 0, strm>>>(p, *na);
-    else if (pl.NR == 4) attn_partial_nested_lds<1, 4><<<wgrid, wblock, 0, strm>>>(p, *na);
+    if (pl.NR == 4) attn_partial_nested_lds<1, 4><<<wgrid, wblock, 0, strm>>>(p, *na);
     else if (pl.NR == 2) attn_partial_nested_lds<1, 2><<<wgrid, wblock, 0, strm>>>(p, *na);
     else attn_partial_nested_lds<1, 1><<<wgrid, wblock, 0, strm>>>(p, *na);
   } else if (pl.kernel == kMfmaStream) {

@@ -173,7 +173,7 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
   // row blocks of a (split, head) read the same K/V; the kernel places them
   // eight workgroups apart, on the same XCD, so the second read is served
   // by that XCD's L2 (llama3_8b_tree partial 23.2 -> 20.6 us).
-  if (pl.kernel == kMfmaLds && pl.RB == 2) {
+  if ((pl.kernel == kMfmaLds || pl.kernel == kMfmaNested) && pl.RB == 2) {
     pl.RB = 1;
     pl.nRB = (tiles + pl.NR - 1) / pl.NR;
   }
