@@ -102,6 +102,8 @@ NESTED = [
     W_("n_r4_padded", B=3, Hq=4, Hkv=4, W=4, ctx_lo=1, ctx_hi=333, masks="tree"),
     W_("n_r48", B=2, Hq=12, Hkv=2, W=8, ctx_lo=33, ctx_hi=517, masks="mixed"),
     W_("n_w64", Hq=4, Hkv=2, W=64, ctx_lo=90, ctx_hi=400, masks="tree", tree_depth=63),
+    # 192 rows per KV head: three row blocks, XCD-paired groups and a tail
+    W_("n_row_blocks3", B=3, Hq=36, Hkv=3, W=16, ctx_lo=100, ctx_hi=1500, masks="mixed"),
     W_("n_segment", Hq=16, Hkv=4, W=16, ctx_lo=15, ctx_hi=260, masks="segment", seg_lookback=1),
     W_("n_ctx_edges", B=4, Hq=8, Hkv=1, W=4, ctx_lo=15, ctx_hi=17),
 ]
