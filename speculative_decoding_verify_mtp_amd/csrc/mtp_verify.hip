@@ -198,7 +198,7 @@ unsigned combine_blocks(const AttnParams& p, const Plan& pl, bool finish, int wa
 // (one row per wave) at most kFinishSplitCUs of them.  The acceptance
 // workgroups run a chain of dependent loads beside the combine, and fewer
 // combine workgroups in flight leave their loads less to queue behind
-// (llama3_8b_tree step 29.7 -> 28.9 us, the other workloads unchanged).
+// (llama3_8b_tree step 29.9 -> 29.3 us, the other workloads unchanged).
 constexpr long kFinishSplitCUs = 128;
 long finish_combine_cus(const AttnParams& p, const Plan& pl) {
   const long free_cus = std::max(1L, (long)kCUs - p.B);
