@@ -33,7 +33,16 @@ from speculative_decoding_verify_mtp_amd import inputs as I  # noqa: E402
 from speculative_decoding_verify_mtp_amd import lib  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "bitnet2b_chain"
+# The headline: the 64-sequence ragged batch (4.9 GB of paged KV), the largest
+# workload and the one whose step is bound by HBM bandwidth.
+DEFAULT_WORKLOAD = "ragged_batch"
+# The first launches of a process over a multi-GB pool run slower (page-table
+# and TLB warm-up: about 20 launches at 1.1-1.3 ms before settling near
+# 0.95 ms on the ragged batch), so at least this many untimed steps run first.
+MIN_WARMUP_STEPS = 24
+# Bytes that stay resident between two reads of one KV replica only if they
+# fit the 256 MB Infinity Cache; a step whose replicas exceed it reads cold.
+MALL_BYTES = 256 << 20
 # The partial kernels and their launch plan: traffic counters taken on other
 # sources are not reported.
 KERNEL_SOURCES = ["attn_lds.hpp", "attn_mfma.hpp", "attn_stream.hpp", "attn_valu.hpp",
@@ -138,38 +147,56 @@ def write_traffic(workload: str, ctr_dir: str) -> int:
     return 0
 
 
-def cpu_baseline(wl: I.Workload, seed: int, budget_s: float) -> dict:
-    """fp64 oracle on a bounded sample: whole steps (attention + acceptance +
-    commit) of the same workload on the host, repeated for about budget_s."""
-    from threadpoolctl import threadpool_info
+def _oracle_steps(wl: I.Workload, seed: int, budget_s: float, threads: int) -> dict:
+    """Whole oracle steps (attention + acceptance + commit) on a bounded sample
+    of the workload, repeated for about budget_s with `threads` BLAS threads."""
+    from threadpoolctl import threadpool_limits
 
     from oracle import verify_oracle as O
 
-    sample = wl
-    # bounded sample: at most 4 sequences of the batch
-    if wl.B > 4:
-        sample = wl.scaled(B=4)
+    sample = wl if wl.B <= 4 else wl.scaled(B=4)  # bounded sample: at most 4 sequences
     inp = I.make_inputs(sample, seed, device="cpu")
     host = inp["host"]
-    f64 = lambda t: t.double().numpy()
+    f64 = lambda t: t.double().numpy()  # noqa: E731
     q, kc, vc = f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"])
     kn, vn = f64(inp["k_new"]), f64(inp["v_new"])
     logits = inp["logits"].numpy()
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        O.verify_attention(q, kc, vc, host["block_table"], host["ctx_lens"], kn, vn,
-                           host["mask_kind"], host["mask_ids"], inp["scale"], wl.seg_lookback)
-        n, path, _ = O.accept(logits, host["draft_ids"], host["mask_kind"], host["mask_ids"])
-        O.kv_commit(kc, vc, kn, vn, n, path, host["block_table"], host["ctx_lens"])
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+    steps = 0
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        while True:
+            O.verify_attention(q, kc, vc, host["block_table"], host["ctx_lens"], kn, vn,
+                               host["mask_kind"], host["mask_ids"], inp["scale"], wl.seg_lookback)
+            n, path, _ = O.accept(logits, host["draft_ids"], host["mask_kind"], host["mask_ids"])
+            O.kv_commit(kc, vc, kn, vn, n, path, host["block_table"], host["ctx_lens"])
+            steps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
     kv = algorithmic_bytes(sample, host["ctx_lens"])["kv"]
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": kv * steps / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{steps} whole oracle steps of {sample.B} sequence(s) of {wl.name} "
                       f"(ctx {host['ctx_lens'].tolist()}) in {dt:.1f} s, fp64 numpy"}
+
+
+def host_cores() -> int:
+    """Cores this process may run on (its affinity mask), at most 16: the
+    share of the host one GPU's job gets."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # not Linux
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl: I.Workload, seed: int, budget_s: float) -> dict:
+    """The fp64 oracle on the host cores: its matmuls and reductions run on a
+    BLAS pool of one thread per core of this process's affinity mask; the
+    paged-cache gather into dense arrays is a single-threaded Python loop."""
+    rec = _oracle_steps(wl, seed, budget_s, host_cores())
+    rec["note"] = ("cores = BLAS threads (the affinity mask, at most 16); the oracle's gather "
+                   "of the paged cache into dense fp64 arrays is single-threaded")
+    return rec
 
 
 def timed_graph(launch, steps: int, warmup: int) -> float:
@@ -589,45 +616,57 @@ def main() -> int:
     # Steps are replayed from HIP graphs: one graph holds NG whole steps (step
     # j reads replica j % R; at least 4 steps, so that the host's graph launch
     # is not counted once per step when a single replica is already cold), a
-    # second holds the NG partial-kernel launches alone, for the per-launch
-    # duration of the dominant kernel.
+    # tail graph the remaining steps % NG, so that exactly --steps steps are
+    # timed.  A third graph holds NG partial-kernel launches alone, for the
+    # per-launch duration of the dominant kernel.
     NG = max(R, 4)
+    reps, tail = divmod(args.steps, NG)
     for r in range(R):  # eager warm-up (also loads the code objects)
         launch_step(r)
     torch.cuda.synchronize()
     g_step, g_part = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    g_tail = torch.cuda.CUDAGraph() if tail else None
     cap = torch.cuda.Stream()
     with torch.cuda.stream(cap):
         with torch.cuda.graph(g_step, stream=cap):
             for j in range(NG):
                 launch_step(j % R)
+        if g_tail is not None:
+            with torch.cuda.graph(g_tail, stream=cap):
+                for j in range(tail):
+                    launch_step(j % R)
         with torch.cuda.graph(g_part, stream=cap):
             for j in range(NG):
                 launch_step(j % R, partial_only=True)
     torch.cuda.synchronize()
 
-    reps = max(1, math.ceil(args.steps / NG))
-    wreps = max(1, math.ceil(args.warmup / NG))
+    warm_steps = max(args.warmup, MIN_WARMUP_STEPS)
+    wreps = math.ceil(warm_steps / NG)
     for _ in range(wreps):
         g_step.replay()
     torch.cuda.synchronize()
-    K = reps * NG
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event after each replay: per-replay step times give the spread
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(reps):
+    marks[0].record()
+    for i in range(reps):
         g_step.replay()
-    e1.record()
+        marks[i + 1].record()
+    if g_tail is not None:
+        g_tail.replay()
+    marks[-1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    step_ms_events = e0.elapsed_time(e1) / K
+    step_ms_events = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_replay = [marks[i].elapsed_time(marks[i + 1]) / NG for i in range(reps)]
 
     # dominant kernel: HIP events around replays of the partial-only graph
+    preps = max(1, math.ceil(args.steps / NG))
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(wreps):
         g_part.replay()
     p0.record()
-    for _ in range(reps):
+    for _ in range(preps):
         g_part.replay()
     p1.record()
     torch.cuda.synchronize()
@@ -635,24 +674,35 @@ def main() -> int:
         print("bench.py: the device reported a data error", file=sys.stderr)
         return 3
 
-    sec_per_step = (t1 - t0) / K
-    partial_ms = p0.elapsed_time(p1) / K
+    sec_per_step = (t1 - t0) / args.steps
+    partial_ms = p0.elapsed_time(p1) / (preps * NG)
     achieved = nbytes["partial"] / (partial_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(wl.name, nbytes["partial"])
+    spread = None
+    if per_replay:
+        q = np.percentile(np.array(per_replay), [10, 50, 90])
+        spread = {"p10": round(float(q[0]), 5), "median": round(float(q[1]), 5),
+                  "p90": round(float(q[2]), 5), "replays": len(per_replay),
+                  "steps_per_replay": NG}
+    reference = achievable_bandwidth(dev, k_all)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, seed, args.cpu_seconds)
+        if wl.B == 1:  # the single-sequence workloads: also one thread
+            cpu["one_thread"] = _oracle_steps(wl, seed, args.cpu_seconds, 1)
 
     mask_desc = {"chain": "chain", "tree": "tree", "segment": f"segment(lookback={wl.seg_lookback})",
                  "mixed": "half chain, half tree"}[wl.masks]
+    cold = R * nbytes["kv"] > MALL_BYTES
     rec = {
         "metric": "verify-step KV GB/s and W-token blocks/sec at 1 GPU; % of HBM roofline",
         "value": round(nbytes["kv"] / sec_per_step / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": wreps * R,
+        "steps": args.steps,
+        "warmup": warm_steps,
+        "warmup_requested": args.warmup,
         "ms_per_step": round(sec_per_step * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -661,23 +711,63 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) K/V/Q, paged KV, shuffled pages)",
         "config": {"workload": wl.name, "B": wl.B, "W": wl.W, "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "D": wl.D, "ctx": [int(ctx.min()), int(ctx.max())], "mask": mask_desc,
-                   "page_size": 16, "kv_replicas": R, "cache": "warm" if R == 1 else "cold",
+                   "page_size": 16, "kv_replicas": R, "cache": "cold" if cold else "warm",
                    "split_tokens": args.split_tokens or "auto"},
         "blocks_per_s": round(wl.B / sec_per_step, 1),
         "ms_per_step_gpu_events": round(step_ms_events, 5),
-        "timing": f"HIP graph replays of {NG} steps (step j reads KV replica j % {R}), wall clock around "
-                  f"{reps} replays; partial kernel from events around a partial-only graph",
+        "ms_per_step_spread": spread,
+        "timing": f"{args.steps} steps: {reps} HIP graph replays of {NG} steps (step j reads KV "
+                  f"replica j % {R}) + a graph of {tail}, after {wreps * NG} untimed steps; "
+                  f"wall clock around the timed replays; partial kernel from events around "
+                  f"{preps} replays of a graph of {NG} partial launches",
         "kv_bytes_per_step": nbytes["kv"],
         "hbm_frac_step": round(nbytes["kv"] / sec_per_step / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "attn_partial (split-K verify attention)",
                      "kernel_us": round(partial_ms * 1e3, 3),
-                     "algorithmic_bytes": nbytes["partial"]},
+                     "algorithmic_bytes": nbytes["partial"],
+                     "launches_timed": preps * NG},
+        "achievable_bandwidth": reference,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def achievable_bandwidth(dev, pool: torch.Tensor) -> dict:
+    """What plain streaming kernels reach on this device, as a reference beside
+    the 8 TB/s peak: a 1 GB device copy (read + write) and a read-only
+    reduction over up to 4 GB of the KV pool (torch's own kernels)."""
+    n = 1 << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    flat = pool.view(-1)
+    flat = flat[: min(flat.numel(), (4 << 30) // flat.element_size())]
+    for _ in range(2):
+        dst.copy_(src)
+        torch.sum(flat, dtype=torch.float32)
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    z.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * reps / (a.elapsed_time(z) * 1e-3) / 1e9
+    a.record()
+    for _ in range(reps):
+        torch.sum(flat, dtype=torch.float32)
+    z.record()
+    torch.cuda.synchronize()
+    read_bytes = flat.numel() * flat.element_size()
+    read_gbs = read_bytes * reps / (a.elapsed_time(z) * 1e-3) / 1e9
+    del src, dst
+    return {"copy_read_plus_write_GBs": round(copy_gbs, 1),
+            "sum_read_GBs": round(read_gbs, 1), "read_bytes": read_bytes,
+            "note": "torch copy_ of 1 GB and torch.sum over the pool, same process, "
+                    "HIP events; a reference for what streaming kernels reach, not a peak"}
 
 
 if __name__ == "__main__":

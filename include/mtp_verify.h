@@ -73,7 +73,8 @@ typedef enum {
   MTP_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
   MTP_ERR_UNSUPPORTED = 3, /* valid but not implemented (D, dtype, page size) */
   MTP_ERR_WORKSPACE = 4,   /* workspace too small */
-  MTP_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+  MTP_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+  MTP_ERR_CONFLICT = 6     /* mtp_check_commit_slots: a commit slot is not the sequence's own */
 } mtp_status;
 
 typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
@@ -382,6 +383,28 @@ mtp_status mtp_build_tree_workspace_size(int32_t B, int32_t K, int32_t V, int32_
 mtp_status mtp_block_positions(const mtp_shape* shape, const int32_t* ctx_lens,
                                const uint8_t* mask_kind, const int32_t* mask_ids,
                                int32_t* positions, void* stream);
+
+/* Host-side check of a block table before commits (no device work; the
+ * arguments are HOST pointers).  The accepted rows of sequence b are written
+ * to the slots of logical positions ctx_lens[b] .. ctx_lens[b] + W - 1, which
+ * the sequence must own alone ("BitMTP" Sec. 3.4 M2: accepted rows are
+ * promoted into the sequence's own workspace slots).  A table that maps one
+ * of those slots a second time, anywhere in logical positions
+ * 0 .. ctx_lens[b'] + W - 1 of any sequence b' (b included), is a caller
+ * error: the commit would race with another sequence's commit or overwrite
+ * history that attention reads, and the device does not detect it.  Pages
+ * shared read-only between sequences (a common prefix) are fine as long as
+ * no commit range reaches them.
+ *   block_table [B, max_pages_per_seq] int32, ctx_lens [B] int32 (host)
+ *   bad_seq     (may be NULL) receives the smallest sequence index involved
+ *               in a conflict, or -1.
+ * Returns MTP_OK, or MTP_ERR_CONFLICT when a conflict exists.  Uses B, W,
+ * num_pages and max_pages_per_seq of `shape`; positions past the table,
+ * unmapped entries and negative contexts are skipped (the device reports
+ * those as data errors).  Time and memory: O(sum of ctx_lens + B W) and
+ * 64 bytes per page. */
+mtp_status mtp_check_commit_slots(const mtp_shape* shape, const int32_t* block_table,
+                                  const int32_t* ctx_lens, int32_t* bad_seq);
 
 /* Reads (and with clear != 0 resets) the current device's sticky status word
  * into *bits.  Synchronous: waits for all work on the device. */

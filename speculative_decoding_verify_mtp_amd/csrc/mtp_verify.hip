@@ -14,6 +14,7 @@
 #include "attn_valu.hpp"
 #include "combine.hpp"
 #include "common.hpp"
+#include "host_checks.hpp"
 #include "hybrid.hpp"
 #include "nested.hpp"
 #include "tree.hpp"
@@ -43,6 +44,7 @@ const char* mtp_status_string(int32_t status) {
     case MTP_ERR_UNSUPPORTED: return "unsupported head dim, dtype or page size";
     case MTP_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MTP_ERR_HIP: return "HIP runtime error at launch";
+    case MTP_ERR_CONFLICT: return "a commit slot is mapped twice or is another sequence's";
     default: return "unknown status";
   }
 }
@@ -201,7 +203,11 @@ unsigned combine_blocks(const AttnParams& p, const Plan& pl, bool finish, int wa
 // (llama3_8b_tree step 29.9 -> 29.3 us, the other workloads unchanged).
 constexpr long kFinishSplitCUs = 128;
 long finish_combine_cus(const AttnParams& p, const Plan& pl) {
-  const long free_cus = std::max(1L, (long)kCUs - p.B);
+  // More sequences than half the compute units: their acceptance workgroups
+  // occupy the chip for a while anyway, and subtracting them would leave the
+  // (looping) combine a handful of workgroups for the whole batch; it keeps
+  // one workgroup per compute unit instead, dispatched behind them.
+  const long free_cus = p.B <= kCUs / 2 ? (long)kCUs - p.B : (long)kCUs;
   return grouped_combine(p, pl, true) ? free_cus : std::min(kFinishSplitCUs, free_cus);
 }
 
@@ -598,6 +604,22 @@ mtp_status mtp_block_positions(const mtp_shape* shape, const int32_t* ctx_lens,
                      static_cast<hipStream_t>(stream)>>>(ctx_lens, mask_kind, mask_ids, positions,
                                                          shape->B, shape->W);
   return launch_status();
+}
+
+mtp_status mtp_check_commit_slots(const mtp_shape* shape, const int32_t* block_table,
+                                  const int32_t* ctx_lens, int32_t* bad_seq) {
+  if (shape == nullptr) return MTP_ERR_NULL;
+  const mtp_shape& s = *shape;
+  if (s.B < 0 || s.W < 1 || s.W > MTP_MAX_W || s.num_pages < 0 || s.max_pages_per_seq < 0)
+    return MTP_ERR_SHAPE;
+  if (bad_seq != nullptr) *bad_seq = -1;
+  if (s.B == 0) return MTP_OK;
+  if (ctx_lens == nullptr || (s.max_pages_per_seq > 0 && block_table == nullptr))
+    return MTP_ERR_NULL;
+  const int32_t bad = first_commit_conflict(s.B, s.W, s.num_pages, s.max_pages_per_seq,
+                                            block_table, ctx_lens);
+  if (bad_seq != nullptr) *bad_seq = bad;
+  return bad < 0 ? MTP_OK : MTP_ERR_CONFLICT;
 }
 
 mtp_status mtp_get_device_status(uint32_t* bits, int32_t clear) {

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libmtpverify.so")
 MTP_F32, MTP_BF16 = 0, 1
 MASK_CHAIN, MASK_TREE, MASK_SEGMENT = 0, 1, 2
 DEV_BAD_MASK, DEV_BAD_CTX, DEV_BAD_PAGE, DEV_BAD_ACCEPT = 1, 2, 4, 8
+MTP_ERR_CONFLICT = 6
 
 EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_size",
            "mtp_verify_attn", "mtp_verify_attn_partial", "mtp_verify_attn_combine",
@@ -28,7 +29,7 @@ EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_si
            "mtp_verify_attn_nested_workspace_size", "mtp_verify_attn_nested",
            "mtp_verify_attn_nested_partial", "mtp_verify_attn_nested_combine",
            "mtp_build_tree", "mtp_build_tree_workspace_size", "mtp_block_positions",
-           "mtp_get_device_status")
+           "mtp_check_commit_slots", "mtp_get_device_status")
 _ATTN_FN = {"both": "mtp_verify_attn", "partial": "mtp_verify_attn_partial",
             "combine": "mtp_verify_attn_combine"}
 _NESTED_FN = {"both": "mtp_verify_attn_nested", "partial": "mtp_verify_attn_nested_partial",
@@ -106,6 +107,8 @@ def load() -> ctypes.CDLL:
     lib.mtp_build_tree_workspace_size.argtypes = [_i32] * 5 + [ctypes.POINTER(_sz)]
     lib.mtp_block_positions.restype = _i32
     lib.mtp_block_positions.argtypes = [sp] + [_vp] * 4 + [_vp]
+    lib.mtp_check_commit_slots.restype = _i32
+    lib.mtp_check_commit_slots.argtypes = [sp, _vp, _vp, ctypes.POINTER(_i32)]
     lib.mtp_get_device_status.restype = _i32
     lib.mtp_get_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i32]
     if lib.mtp_abi_version() != 1:
@@ -340,6 +343,26 @@ def verify_step(q, k_cache, v_cache, block_table, ctx_lens_in, k_new, v_new, mas
         _ptr(accept_path), _ptr(bonus_id), _ptr(ctx_lens_out), int(bool(skip_root)),
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse, accept_len, accept_path, bonus_id, ctx_lens_out
+
+
+def check_commit_slots(block_table, ctx_lens, W: int, num_pages: int) -> int:
+    """Host-side ownership check of the commit slots (mtp_check_commit_slots)
+    on host arrays (numpy or CPU tensors).  Returns the smallest sequence
+    index involved in a conflict, or -1 when every commit slot is its
+    sequence's own."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(np.asarray(block_table), dtype=np.int32)
+    ctx = np.ascontiguousarray(np.asarray(ctx_lens), dtype=np.int32)
+    if bt.ndim != 2 or ctx.shape != (bt.shape[0],):
+        raise ValueError("block_table must be [B, max_pages] and ctx_lens [B]")
+    cs = Shape(bt.shape[0], W, 1, 1, 64, 16, num_pages, bt.shape[1], 0, MTP_F32, 0.0, -1, 0)
+    bad = ctypes.c_int32(-2)
+    st = load().mtp_check_commit_slots(ctypes.byref(cs), bt.ctypes.data, ctx.ctypes.data,
+                                       ctypes.byref(bad))
+    if st not in (0, MTP_ERR_CONFLICT):
+        _check("mtp_check_commit_slots", st)
+    return int(bad.value)
 
 
 def device_status(clear: bool = True) -> int:

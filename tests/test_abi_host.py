@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function(L):
 
 def test_abi_version_and_status_strings(L):
     assert L.mtp_abi_version() == 1
-    for code in range(6):
+    for code in range(7):
         assert L.mtp_status_string(code).decode()
     assert L.mtp_status_string(99).decode() == "unknown status"
 
@@ -212,3 +212,101 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         lib.load()
+
+
+# ----------------------------------------------------------------------------
+# commit-slot ownership (host-side check, no device work)
+# ----------------------------------------------------------------------------
+
+def brute_commit_conflict(table, ctx, W, num_pages) -> int:
+    """Smallest sequence index in a pair (b, b') where a slot of b's commit
+    range [ctx_b, ctx_b + W) is also mapped in b''s range [0, ctx_b' + W)
+    (b' = b: at a second logical position).  Sets of slots, pair by pair."""
+    B, maxp = table.shape
+
+    def slots(b, lo, hi):
+        out = []
+        for t in range(max(lo, 0), min(hi, 16 * maxp)):
+            p = int(table[b, t // 16])
+            if 0 <= p < num_pages:
+                out.append((p, t % 16))
+        return out
+
+    bad = -1
+    for b in range(B):
+        if ctx[b] < 0:
+            continue
+        mine = slots(b, ctx[b], ctx[b] + W)
+        for b2 in range(B):
+            if ctx[b2] < 0 and b2 != b:
+                theirs = []
+            else:
+                theirs = slots(b2, 0, (ctx[b2] if ctx[b2] >= 0 else 0) + W)
+            if b2 == b:  # a commit slot at a second logical position
+                hit = any(theirs.count(x) > 1 for x in mine)
+            else:
+                hit = bool(set(mine) & set(theirs))
+            if hit and (bad < 0 or min(b, b2) < bad):
+                bad = min(b, b2)
+    return bad
+
+
+def test_commit_slots_of_the_generated_workloads_are_owned(L):
+    from speculative_decoding_verify_mtp_amd import inputs as I
+    for name in ("bitnet2b_chain", "lca_segments", "ragged_batch"):
+        st = I.make_structure(I.WORKLOADS[name], I.workload_seed(name))
+        assert lib.check_commit_slots(st["block_table"], st["ctx_lens"], I.WORKLOADS[name].W,
+                                      st["num_pages"]) == -1, name
+
+
+def test_commit_slot_conflicts_are_reported(L):
+    import numpy as np
+    W, pages = 8, 12
+    # three sequences, ctx 20, 40, 5: pages [0,1], [2,3,4], [5]
+    table = np.array([[0, 1, -1], [2, 3, 4], [5, -1, -1]], dtype=np.int32)
+    ctx = np.array([20, 40, 5], dtype=np.int32)
+    assert lib.check_commit_slots(table, ctx, W, pages) == -1
+    # a read-only shared prefix page (both commit elsewhere) is fine
+    shared = table.copy()
+    shared[1, 0] = 0
+    assert lib.check_commit_slots(shared, ctx, W, pages) == -1
+    # sequence 2 commits into a page sequence 0 commits into
+    t = table.copy()
+    t[2, 0] = 1
+    assert lib.check_commit_slots(t, ctx, W, pages) == 0
+    # sequence 2 commits into sequence 1's history (page 2 holds tokens 0..15)
+    t = table.copy()
+    t[2, 0] = 2
+    assert lib.check_commit_slots(t, ctx, W, pages) == 1
+    # sequence 1 maps one page twice: its commit overwrites its own history
+    t = table.copy()
+    t[1, 2] = 2
+    assert lib.check_commit_slots(t, ctx, W, pages) == 1
+    # a commit range that runs past the table or into unmapped entries is
+    # left to the device (reported there as a data error)
+    t = table.copy()
+    t[0, 1] = -1
+    assert lib.check_commit_slots(t, ctx, W, pages) == -1
+
+
+def test_commit_slot_check_matches_brute_force(L):
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        B = int(rng.integers(1, 6))
+        W = int(rng.integers(1, 20))
+        num_pages = int(rng.integers(1, 14))
+        maxp = int(rng.integers(1, 5))
+        table = rng.integers(-1, num_pages + 1, size=(B, maxp)).astype(np.int32)
+        ctx = rng.integers(-2, 16 * maxp + 1, size=B).astype(np.int32)
+        want = brute_commit_conflict(table, ctx, W, num_pages)
+        assert lib.check_commit_slots(table, ctx, W, num_pages) == want, (trial, table, ctx, W)
+
+
+def test_commit_slot_check_argument_errors(L):
+    s = shape(W=0)
+    assert L.mtp_check_commit_slots(ctypes.byref(s), None, None, None) == 2
+    s = shape()
+    assert L.mtp_check_commit_slots(ctypes.byref(s), None, None, None) == 1
+    s = shape(B=0)
+    assert L.mtp_check_commit_slots(ctypes.byref(s), None, None, None) == 0

@@ -2,10 +2,10 @@
 
 Attention within |d| <= 1e-3 + 1e-2 |ref| elementwise (bf16 inputs) or
 1e-4 + 1e-4 |ref| (fp32 inputs); acceptance, paths, bonus ids, context
-lengths and committed K/V bytes bit-exact.  Small cases span several 32-key
-tiles, several splits and ragged tails; the five full-size workloads run in
-the launch configuration the benchmark uses (sampled sequences for the
-ragged batch).
+lengths and committed K/V bytes bit-exact.  Cases span several 32-key
+tiles, several splits and ragged tails, more than 64 splits per row, equal-
+depth tree ties and the finish launch with more sequences than compute units
+can take beside it.  The five full-size workloads are in test_gpu_full_size.py.
 """
 from __future__ import annotations
 
@@ -13,9 +13,8 @@ import numpy as np
 import pytest
 import torch
 
-from tests.gpu_common import (I, O, lib, assert_accept_equal, assert_attn_close, banner, f64,
-                              gpu_inputs, ints, oracle_accept, oracle_attn, oracle_attn_sub, raw,
-                              run_attn, sub_problem, tol_for)
+from tests.gpu_common import (I, O, lib, assert_accept_equal, assert_attn_close, f64, gpu_inputs,
+                              ints, oracle_accept, oracle_attn, raw, run_attn, tol_for)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.filterwarnings("ignore::RuntimeWarning"),
@@ -172,43 +171,39 @@ def test_loose_max_ctx_len_bound():
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl))
 
 
-FULL = ["tiny_chain", "bitnet2b_chain", "llama3_8b_tree", "lca_segments"]
+# More than 64 splits per row: the combines' loop past their first 64 splits
+# (the automatic plan reaches it for one sequence of 64K tokens, as 128
+# splits of 512).  ctx 5000 with 64-token splits gives 79 splits.
+MANY_SPLITS = [
+    W_("splits79_lds", B=1, Hq=20, Hkv=5, W=8, ctx_lo=5000, ctx_hi=5000),
+    W_("splits79_d64", B=1, Hq=16, Hkv=4, D=64, W=16, ctx_lo=5000, ctx_hi=5000,
+       masks="segment", seg_lookback=1),
+    W_("splits79_valu", B=1, Hq=4, Hkv=2, W=3, ctx_lo=5000, ctx_hi=5000, masks="tree"),
+    W_("splits79_fp32", B=2, Hq=4, Hkv=4, D=64, W=4, dtype="f32", ctx_lo=4990, ctx_hi=5000),
+]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_workloads(name):
-    wl = I.WORKLOADS[name]
-    inp = gpu_inputs(wl, I.workload_seed(name))
-    out, lse = run_attn(inp)
+@pytest.mark.parametrize("wl", MANY_SPLITS, ids=[w.name for w in MANY_SPLITS])
+def test_more_than_64_splits(wl):
+    inp = gpu_inputs(wl, 19)
     ref_out, ref_lse = oracle_attn(inp)
-    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=name)
-    assert_accept_equal(lib.accept(inp["logits"], inp["draft_ids"], inp["mask_kind"],
-                                   inp["mask_ids"]), oracle_accept(inp))
-
-
-def test_full_size_lca_with_fig2_lookback():
-    wl = I.WORKLOADS["lca_segments"].scaled(seg_lookback=1)
-    inp = gpu_inputs(wl, I.workload_seed("lca_segments"))
-    out, lse = run_attn(inp)
-    ref_out, ref_lse = oracle_attn(inp)
-    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what="lca lookback 1")
-
-
-def test_full_size_ragged_batch_sampled():
-    name = "ragged_batch"
-    wl = I.WORKLOADS[name]
-    inp = gpu_inputs(wl, I.workload_seed(name))
-    out, lse = run_attn(inp)
-    ctx = inp["host"]["ctx_lens"]
-    # the longest and shortest sequence, plus a chain and a tree from the middle
-    seqs = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 10, 21})
-    banner(f"ragged sample {seqs} ctx={[int(ctx[s]) for s in seqs]}")
-    sub = sub_problem(inp, seqs)
-    ref_out, ref_lse = oracle_attn_sub(sub)
-    sel = torch.tensor(seqs, device=out.device)
-    assert_attn_close(out[sel], lse[sel], ref_out, ref_lse, *tol_for(wl), what=name)
-    assert_accept_equal(lib.accept(inp["logits"], inp["draft_ids"], inp["mask_kind"],
-                                   inp["mask_ids"]), oracle_accept(inp))
+    out, lse = run_attn(inp, split_tokens=64)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"{wl.name} attn")
+    n_ref, path_ref, bonus_ref = oracle_accept(inp)
+    kc_ref, vc_ref, ctx_ref = O.kv_commit(raw(inp["k_cache"]), raw(inp["v_cache"]),
+                                          raw(inp["k_new"]), raw(inp["v_new"]), n_ref, path_ref,
+                                          ints(inp["block_table"]), ints(inp["ctx_lens"]))
+    out, lse, n, path, bonus, ctx_out = lib.verify_step(
+        inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["ctx_lens"],
+        inp["k_new"], inp["v_new"], inp["mask_kind"], inp["mask_ids"], inp["logits"],
+        inp["draft_ids"], max_ctx_len=int(inp["host"]["ctx_lens"].max()), scale=inp["scale"],
+        seg_lookback=inp["seg_lookback"], split_tokens=64)
+    torch.cuda.synchronize()
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"{wl.name} step")
+    assert_accept_equal((n, path, bonus), (n_ref, path_ref, bonus_ref))
+    assert np.array_equal(ints(ctx_out), ctx_ref)
+    assert np.array_equal(raw(inp["k_cache"]), kc_ref)
+    assert np.array_equal(raw(inp["v_cache"]), vc_ref)
 
 
 # ----------------------------------------------------------------------------
@@ -252,6 +247,60 @@ def test_accept_argmax_ties_take_the_smallest_id():
     got = lib.accept(logits.cuda(), draft.cuda(), kinds.cuda(), ids.cuda())
     assert_accept_equal(got, ref)
     assert list(ints(got[0])) == [3, 1, 3]
+
+
+def tie_block(tgt: np.ndarray, V: int):
+    """Four tree blocks of width 8 whose siblings share drafted ids, so that
+    several equally deep nodes are accepted.  Returns (parents, drafts,
+    expected paths).  A draft that must not match takes its parent's target
+    + 1 (mod V)."""
+    par = np.array([[-1, 0, 0, 1, 2, 1, 2, 3],
+                    [-1, 0, 0, 1, 2, 1, 2, 3],
+                    [-1, 0, 0, 1, 2, 1, 2, 3],
+                    [-1, 0, 0, 2, 1, 4, 3, 6]], dtype=np.int32)
+    # per block: the nodes whose draft equals their parent's target
+    match = [{1, 2, 3, 4},        # depth-2 nodes 3 and 4 tie: node 3
+             {1, 2, 4, 6},        # depth-2 nodes 4 and 6 tie: node 4
+             {1, 2, 3, 4, 7},     # node 7 is deeper: depth 3 beats the tie
+             {1, 2, 3, 4, 6}]     # 3 (under 2) and 4 (under 1) tie at depth 2,
+    #                               6 under 3 is deeper: node 6
+    paths = [[0, 1, 3], [0, 2, 4], [0, 1, 3, 7], [0, 2, 3, 6]]
+    draft = np.full(par.shape, -1, dtype=np.int32)
+    for b in range(par.shape[0]):
+        for i in range(1, par.shape[1]):
+            want = int(tgt[b, par[b, i]])
+            draft[b, i] = want if i in match[b] else (want + 1) % V
+    return par, draft, paths
+
+
+def test_accept_equal_depth_ties_take_the_smallest_node():
+    """Siblings sharing a drafted id both match; of equally deep accepted
+    nodes the one with the smallest index wins (acceptance alone, and inside
+    the step's finish launch with its commit)."""
+    wl = W_("acc_ties", B=4, Hq=8, Hkv=2, W=8, ctx_lo=20, ctx_hi=60, masks="tree")
+    inp = gpu_inputs(wl, 31)
+    par, draft, paths = tie_block(inp["host"]["target_ids"], wl.vocab)
+    inp["mask_ids"] = torch.from_numpy(par).cuda()
+    inp["draft_ids"] = torch.from_numpy(draft).cuda()
+    ref = oracle_accept(inp)
+    for b, p in enumerate(paths):
+        assert list(ref[1][b][:len(p)]) == p and ref[0][b] == len(p) - 1
+    assert_accept_equal(lib.accept(inp["logits"], inp["draft_ids"], inp["mask_kind"],
+                                   inp["mask_ids"]), ref)
+    ref_out, ref_lse = oracle_attn(inp)
+    kc_ref, vc_ref, ctx_ref = O.kv_commit(raw(inp["k_cache"]), raw(inp["v_cache"]),
+                                          raw(inp["k_new"]), raw(inp["v_new"]), ref[0], ref[1],
+                                          ints(inp["block_table"]), ints(inp["ctx_lens"]))
+    out, lse, n, path, bonus, ctx_out = lib.verify_step(
+        inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["ctx_lens"],
+        inp["k_new"], inp["v_new"], inp["mask_kind"], inp["mask_ids"], inp["logits"],
+        inp["draft_ids"], max_ctx_len=int(inp["host"]["ctx_lens"].max()), scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what="ties")
+    assert_accept_equal((n, path, bonus), ref)
+    assert np.array_equal(ints(ctx_out), ctx_ref)
+    assert np.array_equal(raw(inp["k_cache"]), kc_ref)
+    assert np.array_equal(raw(inp["v_cache"]), vc_ref)
 
 
 # ----------------------------------------------------------------------------
@@ -515,6 +564,10 @@ STEP = [
     W_("step_segment_d64", B=3, Hq=16, Hkv=16, D=64, W=16, ctx_lo=30, ctx_hi=300,
        masks="segment", seg_lookback=1),
     W_("step_fp32", B=2, Hq=4, Hkv=4, D=64, W=4, dtype="f32", ctx_lo=100, ctx_hi=256),
+    # more sequences than half the compute units: the finish launch keeps one
+    # combine workgroup per compute unit behind the acceptance workgroups
+    W_("step_b300", B=300, Hq=8, Hkv=2, W=16, ctx_lo=0, ctx_hi=64, masks="mixed",
+       spare_pages=8),
 ]
 
 

@@ -126,3 +126,13 @@ def test_positions_of_a_tree_are_depths_from_the_golden_tree():
 def test_positions_of_a_malformed_mask_are_minus_one():
     pos = O.block_positions([5], [O.TREE], np.array([[-1, 0, 2]]))
     assert np.all(pos == -1)
+
+
+def test_golden_tree_one_token_vocabulary():
+    """V = 1: pruning leaves no candidate at any depth (hand-worked fixture)."""
+    g = load_golden("dynamic_tree_v1.txt")
+    p = np.array([g["probs"]], dtype=np.float32)
+    for thr in (0.0, 0.5):
+        d, par, dep, n = O.dynamic_tree(p, [g["root"]], g["W"], g["n_mask"], thr)
+        assert list(d[0]) == g["draft"] and list(par[0]) == g["parents"]
+        assert list(dep[0]) == g["depth"] and n[0] == g["n_nodes"]
