@@ -74,7 +74,8 @@ typedef enum {
   MTP_ERR_UNSUPPORTED = 3, /* valid but not implemented (D, dtype, page size) */
   MTP_ERR_WORKSPACE = 4,   /* workspace too small */
   MTP_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
-  MTP_ERR_CONFLICT = 6     /* mtp_check_commit_slots: a commit slot is not the sequence's own */
+  MTP_ERR_CONFLICT = 6,    /* mtp_check_commit_slots: a commit slot is not the sequence's own */
+  MTP_ERR_SCRATCH = 7      /* mtp_verify_step_noalloc: the shape exceeds the fixed scratch */
 } mtp_status;
 
 typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
@@ -255,6 +256,27 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
                            int32_t* accept_len, int32_t* accept_path, int32_t* bonus_id,
                            int32_t* ctx_lens_out, int32_t skip_root, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* mtp_verify_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same launches and results, with the split-K partials in a fixed
+ * 64 MiB array the library keeps in device memory (each GPU the library
+ * runs on holds its own copy until the process ends) instead of a caller
+ * workspace.  The caller still passes every input and output; nothing is
+ * allocated and no part of the array needs clearing.  A shape whose
+ * mtp_verify_attn_workspace_size exceeds 64 MiB returns MTP_ERR_SCRATCH and
+ * enqueues nothing (the five reference workloads need at most 34 MB).  All
+ * calls on one GPU share its array: calls that may overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.
+ * Arguments and errors otherwise as for mtp_verify_step. */
+mtp_status mtp_verify_step_noalloc(const mtp_shape* shape, const void* q, void* k_cache,
+                                   void* v_cache, const int32_t* block_table,
+                                   const int32_t* ctx_lens_in, const void* k_new,
+                                   const void* v_new, const uint8_t* mask_kind,
+                                   const int32_t* mask_ids, const float* logits, int32_t V,
+                                   const int32_t* draft_ids, float* out, float* lse,
+                                   int32_t* accept_len, int32_t* accept_path, int32_t* bonus_id,
+                                   int32_t* ctx_lens_out, int32_t skip_root, void* stream);
 
 /* ---- Nested KV4 / KV8 cache ("BitNest: Bit-Nested Speculative Decoding for
  * Memory-Efficient LLM Inference Acceleration", Sec. 3.4 and Sec. A.2) ----

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -45,6 +46,7 @@ const char* mtp_status_string(int32_t status) {
     case MTP_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MTP_ERR_HIP: return "HIP runtime error at launch";
     case MTP_ERR_CONFLICT: return "a commit slot is mapped twice or is another sequence's";
+    case MTP_ERR_SCRATCH: return "the shape needs more than the library's fixed 64 MiB device scratch";
     default: return "unknown status";
   }
 }
@@ -429,6 +431,70 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
       finish_kernel<64, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);
   }
   return launch_status();
+}
+
+}  // extern "C"
+
+// ---- the step without a caller workspace ----------------------------------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid hipMalloc): the step's
+// split-K partials go to this file-scope device array instead of a caller
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: host code uses only the address hipGetSymbolAddress
+// returns on each device, taken once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device
+
+mtp_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MTP_ERR_HIP;
+  if (dev >= kMaxScratchDevices) return MTP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MTP_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mtp_status mtp_verify_step_noalloc(const mtp_shape* shape, const void* q, void* k_cache,
+                                   void* v_cache, const int32_t* block_table,
+                                   const int32_t* ctx_lens_in, const void* k_new,
+                                   const void* v_new, const uint8_t* mask_kind,
+                                   const int32_t* mask_ids, const float* logits, int32_t V,
+                                   const int32_t* draft_ids, float* out, float* lse,
+                                   int32_t* accept_len, int32_t* accept_path, int32_t* bonus_id,
+                                   int32_t* ctx_lens_out, int32_t skip_root, void* stream) {
+  // the size check comes first and needs no device
+  const mtp_status st = check_shape(shape);
+  if (st != MTP_OK) return st;
+  const Plan pl = make_plan(*shape);
+  if (pl.seg_offset + pl.seg_bytes > kScratchBytes) return MTP_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (shape->B > 0) {
+    const mtp_status ss = scratch_of_current_device(&ws);
+    if (ss != MTP_OK) return ss;
+  }
+  // Nothing in the scratch needs to start at zero: the partial launch writes
+  // every partial and segment record the combine reads.
+  return mtp_verify_step(shape, q, k_cache, v_cache, block_table, ctx_lens_in, k_new, v_new,
+                         mask_kind, mask_ids, logits, V, draft_ids, out, lse, accept_len,
+                         accept_path, bonus_id, ctx_lens_out, skip_root, ws,
+                         ws != nullptr ? kScratchBytes : 0, stream);
 }
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libmtpverify.so")
 MTP_F32, MTP_BF16 = 0, 1
 MASK_CHAIN, MASK_TREE, MASK_SEGMENT = 0, 1, 2
 DEV_BAD_MASK, DEV_BAD_CTX, DEV_BAD_PAGE, DEV_BAD_ACCEPT = 1, 2, 4, 8
-MTP_ERR_CONFLICT = 6
+MTP_ERR_CONFLICT, MTP_ERR_SCRATCH = 6, 7
 
 EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_size",
            "mtp_verify_attn", "mtp_verify_attn_partial", "mtp_verify_attn_combine",
@@ -29,7 +29,7 @@ EXPORTS = ("mtp_abi_version", "mtp_status_string", "mtp_verify_attn_workspace_si
            "mtp_verify_attn_nested_workspace_size", "mtp_verify_attn_nested",
            "mtp_verify_attn_nested_partial", "mtp_verify_attn_nested_combine",
            "mtp_build_tree", "mtp_build_tree_workspace_size", "mtp_block_positions",
-           "mtp_check_commit_slots", "mtp_get_device_status")
+           "mtp_check_commit_slots", "mtp_verify_step_noalloc", "mtp_get_device_status")
 _ATTN_FN = {"both": "mtp_verify_attn", "partial": "mtp_verify_attn_partial",
             "combine": "mtp_verify_attn_combine"}
 _NESTED_FN = {"both": "mtp_verify_attn_nested", "partial": "mtp_verify_attn_nested_partial",
@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
                                       + [_i32, _vp, _vp, _vp])
     lib.mtp_verify_step.restype = _i32
     lib.mtp_verify_step.argtypes = ([sp] + [_vp] * 10 + [_i32] + [_vp] * 7 + [_i32, _vp, _sz, _vp])
+    lib.mtp_verify_step_noalloc.restype = _i32
+    lib.mtp_verify_step_noalloc.argtypes = [sp] + [_vp] * 10 + [_i32] + [_vp] * 7 + [_i32, _vp]
     npp = ctypes.POINTER(NestedKVStruct)
     lib.mtp_kv_quantize.restype = _i32
     lib.mtp_kv_quantize.argtypes = [sp, _vp, _vp, _i32, _vp, npp, _vp]
@@ -312,9 +314,11 @@ def verify_step(q, k_cache, v_cache, block_table, ctx_lens_in, k_new, v_new, mas
                 logits, draft_ids, *, out=None, lse=None, want_lse=True, accept_len=None,
                 accept_path=None, bonus_id=None, ctx_lens_out=None, skip_root=False,
                 workspace=None, shape=None, max_ctx_len=None, scale=0.0, seg_lookback=-1,
-                split_tokens=0, stream=None):
+                split_tokens=0, stream=None, noalloc=False):
     """The whole verify step (attention, acceptance, commit) in two launches.
 
+    noalloc=True calls mtp_verify_step_noalloc (the library's fixed device
+    scratch instead of a workspace; `workspace` must then be None).
     Returns (out, lse, accept_len, accept_path, bonus_id, ctx_lens_out)."""
     lib = load()
     if shape is None:
@@ -327,7 +331,9 @@ def verify_step(q, k_cache, v_cache, block_table, ctx_lens_in, k_new, v_new, mas
         out = torch.empty((B, W, Hq, D), dtype=torch.float32, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((B, W, Hq), dtype=torch.float32, device=dev)
-    if workspace is None:
+    if noalloc and workspace is not None:
+        raise ValueError("noalloc=True takes no workspace")
+    if workspace is None and not noalloc:
         workspace = torch.empty(max(workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
     accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
     accept_path = (torch.empty((B, W), dtype=torch.int32, device=dev) if accept_path is None
@@ -336,12 +342,15 @@ def verify_step(q, k_cache, v_cache, block_table, ctx_lens_in, k_new, v_new, mas
     if ctx_lens_out is None:
         ctx_lens_out = torch.empty_like(ctx_lens_in)
     cs = shape.c()
-    _check("mtp_verify_step", lib.mtp_verify_step(
-        ctypes.byref(cs), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        _ptr(ctx_lens_in), _ptr(k_new), _ptr(v_new), _ptr(mask_kind), _ptr(mask_ids),
-        _ptr(logits), V, _ptr(draft_ids), _ptr(out), _ptr(lse), _ptr(accept_len),
-        _ptr(accept_path), _ptr(bonus_id), _ptr(ctx_lens_out), int(bool(skip_root)),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+    args = (ctypes.byref(cs), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(ctx_lens_in), _ptr(k_new), _ptr(v_new), _ptr(mask_kind), _ptr(mask_ids),
+            _ptr(logits), V, _ptr(draft_ids), _ptr(out), _ptr(lse), _ptr(accept_len),
+            _ptr(accept_path), _ptr(bonus_id), _ptr(ctx_lens_out), int(bool(skip_root)))
+    if noalloc:
+        _check("mtp_verify_step_noalloc", lib.mtp_verify_step_noalloc(*args, _stream(stream)))
+    else:
+        _check("mtp_verify_step", lib.mtp_verify_step(*args, _ptr(workspace), workspace.numel(),
+                                                      _stream(stream)))
     return out, lse, accept_len, accept_path, bonus_id, ctx_lens_out
 
 

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function(L):
 
 def test_abi_version_and_status_strings(L):
     assert L.mtp_abi_version() == 1
-    for code in range(7):
+    for code in range(8):
         assert L.mtp_status_string(code).decode()
     assert L.mtp_status_string(99).decode() == "unknown status"
 
@@ -310,3 +310,17 @@ def test_commit_slot_check_argument_errors(L):
     assert L.mtp_check_commit_slots(ctypes.byref(s), None, None, None) == 1
     s = shape(B=0)
     assert L.mtp_check_commit_slots(ctypes.byref(s), None, None, None) == 0
+
+
+def test_noalloc_step_checks_its_scratch_limit_on_the_host(L):
+    """mtp_verify_step_noalloc rejects a shape whose partials exceed its fixed
+    64 MiB scratch before it touches a device (and B = 0 is a no-op)."""
+    big = shape(B=1024, W=64, Hq=64, Hkv=8, num_pages=100, max_pages_per_seq=4096,
+                max_ctx_len=65536)
+    st, n = ws(L, big)
+    assert st == 0 and n > 64 << 20
+    args = [None] * 10 + [1000] + [None] * 7 + [0, None]  # V = 1000
+    assert L.mtp_verify_step_noalloc(ctypes.byref(big), *args) == lib.MTP_ERR_SCRATCH
+    empty = shape(B=0)
+    assert L.mtp_verify_step_noalloc(ctypes.byref(empty), *args) == 0
+    assert L.mtp_verify_step_noalloc(ctypes.byref(shape(W=0)), *args) == 2
