@@ -14,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmtpverify.so")
+# measurement helper (a plain streaming read), built beside the library
+PROBE_LIB = os.path.join(PKG, "libmtpprobe.so")
 ARCH = "gfx950"
 
 
@@ -27,23 +29,21 @@ def hipcc() -> str:
     return found
 
 
-def command(out: str = LIB) -> list[str]:
+def command(out: str = LIB, source: str = "mtp_verify.hip") -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # keep the compiler from forming packed fp32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", f"-I{CSRC}",
-        os.path.join(CSRC, "mtp_verify.hip"),
+        os.path.join(CSRC, source),
         "-o", out,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles the library (always, also when one is already there) and
-    returns its path.  The new file replaces the old one atomically."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def _compile(out: str, source: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
+    cmd = command(tmp, source)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
@@ -53,7 +53,15 @@ def build(verbose: bool = False) -> str:
         text = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
         if text.strip():
             sys.stderr.write(text + "\n")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles the library and the read probe (always, also when they are
+    already there) and returns the library's path.  Each new file replaces
+    the old one atomically."""
+    _compile(LIB, "mtp_verify.hip", verbose)
+    _compile(PROBE_LIB, "read_probe.hip", verbose)
     return LIB
 
 

@@ -324,3 +324,20 @@ def test_noalloc_step_checks_its_scratch_limit_on_the_host(L):
     empty = shape(B=0)
     assert L.mtp_verify_step_noalloc(ctypes.byref(empty), *args) == 0
     assert L.mtp_verify_step_noalloc(ctypes.byref(shape(W=0)), *args) == 2
+
+
+def test_read_probe_library_exports_and_checks_arguments(L):
+    """The measurement helper beside the library (include/mtp_probe.h)."""
+    assert os.path.exists(B.PROBE_LIB)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(B.ROOT, "include", "mtp_probe.h")).read(),
+                  flags=re.S)
+    assert sorted(set(re.findall(r"\b(mtp_[a-z_]+)\s*\(", text))) == ["mtp_probe_stream_read"]
+    out = os.popen(f"nm -D --defined-only {B.PROBE_LIB}").read()
+    assert re.search(r"\bT mtp_probe_stream_read\b", out)
+    P = ctypes.CDLL(B.PROBE_LIB)
+    P.mtp_probe_stream_read.restype = ctypes.c_int32
+    P.mtp_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    assert P.mtp_probe_stream_read(None, 16, None, None) == 1
+    assert P.mtp_probe_stream_read(16, 17, 16, None) == 2  # size not a multiple of 16
+    assert P.mtp_probe_stream_read(8, 16, 16, None) == 2  # misaligned
