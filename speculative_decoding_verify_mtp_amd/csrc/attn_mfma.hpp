@@ -100,21 +100,13 @@ struct MfmaState {
 // relative to the reference stay below 2^8, far from fp32 overflow.
 constexpr float kRescaleSlack = 8.f;
 
-// One 32-key tile: scores, online-softmax update, PV accumulate.
-// kf: K operands of the two 16-key halves; vv: V vectors of keys
-// {4q..4q+3, 16+4q..16+4q+3}; vis(k, e) tells whether row tile k may see key
-// e of this lane's 8 keys.
-template <int D, int RB, typename VisFn>
-__device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
-                                          const bf16x8 (&kf)[2][D / 32],
-                                          const VRow<D> (&vv)[8], float scale_log2,
-                                          MfmaState<D, RB>& st, VisFn vis) {
+// Raw scores of one 32-key tile for the RB row tiles: x[k][e] = q . k of
+// this lane's row of tile k and its e-th key (keys {4q..4q+3} of the first
+// 16-key half, then the same of the second), unscaled.
+template <int D, int RB>
+__device__ __forceinline__ void tile_scores(const bf16x8 (&qf)[RB][D / 32],
+                                            const bf16x8 (&kf)[2][D / 32], float (&x)[RB][8]) {
   constexpr int NC = D / 32;
-  constexpr int NT = D / 16;
-  // P is split into bf16 hi + lo parts (two PV products): one bf16 rounding
-  // of P alone costs up to 2^-9 relative per weight, which exceeds the
-  // 1e-3 + 1e-2|ref| bound on short or peaked rows; hi + lo keeps ~16 bits.
-  bf16x8 pf[RB], pl[RB];
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -123,18 +115,35 @@ __device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][m], qf[k][m], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][m], qf[k][m], s1, 0, 0, 0);
     }
-    // raw scores; the scale (> 0) is applied after the max and inside the exp
-    float x[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[e] = s0[e];
-      x[4 + e] = s1[e];
+      x[k][e] = s0[e];
+      x[k][4 + e] = s1[e];
     }
+  }
+}
+
+// Online-softmax update of one 32-key tile from its raw scores: the running
+// max and sum of each row tile, the rescale of its accumulators when the
+// reference max moves, and the tile's probabilities as the PV product's
+// operand (P^T, bf16 hi + lo parts).  vis(k, e) tells whether row tile k may
+// see key e of this lane's 8 keys.
+template <int D, int RB, typename VisFn>
+__device__ __forceinline__ void tile_softmax(float (&x)[RB][8], float scale_log2,
+                                             MfmaState<D, RB>& st, bf16x8 (&pf)[RB],
+                                             bf16x8 (&pl)[RB], VisFn vis) {
+  constexpr int NT = D / 16;
+  // P is split into bf16 hi + lo parts (two PV products): one bf16 rounding
+  // of P alone costs up to 2^-9 relative per weight, which exceeds the
+  // 1e-3 + 1e-2|ref| bound on short or peaked rows; hi + lo keeps ~16 bits.
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    // raw scores; the scale (> 0) is applied after the max and inside the exp
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (!vis(k, e)) x[e] = neg_inf();
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      if (!vis(k, e)) x[k][e] = neg_inf();
+    float mx = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
+                     fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
     mx = rows4_max(mx);
     mx *= scale_log2;
     const float mold = st.m[k];
@@ -144,7 +153,7 @@ __device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
     __bf16 ph[8], plo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(fmaf(x[e], scale_log2, -muse));
+      const float pe = fast_exp2(fmaf(x[k][e], scale_log2, -muse));
       sum += pe;
       ph[e] = (__bf16)pe;
       plo[e] = (__bf16)(pe - (float)ph[e]);
@@ -160,6 +169,14 @@ __device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
     __builtin_memcpy(&pf[k], ph, sizeof(bf16x8));
     __builtin_memcpy(&pl[k], plo, sizeof(bf16x8));
   }
+}
+
+// PV accumulate of one 32-key tile: acc^T += V^T P^T for the hi and the lo
+// part of P.  vv: V vectors of keys {4q..4q+3, 16+4q..16+4q+3}.
+template <int D, int RB>
+__device__ __forceinline__ void tile_pv(const bf16x8 (&pf)[RB], const bf16x8 (&pl)[RB],
+                                        const VRow<D> (&vv)[8], MfmaState<D, RB>& st) {
+  constexpr int NT = D / 16;
 #define MTPV_PV_STEP(T)                                                                 \
   if constexpr ((T) < NT) {                                                            \
     const bf16x8 a = pack_v_operand<D, (T)>(vv);                                       \
@@ -179,6 +196,22 @@ __device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
   MTPV_PV_STEP(6)
   MTPV_PV_STEP(7)
 #undef MTPV_PV_STEP
+}
+
+// One 32-key tile: scores, online-softmax update, PV accumulate.
+// kf: K operands of the two 16-key halves; vv: V vectors of keys
+// {4q..4q+3, 16+4q..16+4q+3}; vis(k, e) tells whether row tile k may see key
+// e of this lane's 8 keys.
+template <int D, int RB, typename VisFn>
+__device__ __forceinline__ void mfma_tile(const bf16x8 (&qf)[RB][D / 32],
+                                          const bf16x8 (&kf)[2][D / 32],
+                                          const VRow<D> (&vv)[8], float scale_log2,
+                                          MfmaState<D, RB>& st, VisFn vis) {
+  float x[RB][8];
+  tile_scores<D, RB>(qf, kf, x);
+  bf16x8 pf[RB], pl[RB];
+  tile_softmax<D, RB>(x, scale_log2, st, pf, pl, vis);
+  tile_pv<D, RB>(pf, pl, vv, st);
 }
 
 // Key index (0..31) inside a 32-key tile of this lane's e-th PV key.

@@ -36,7 +36,12 @@
 
 namespace mtpv {
 
-constexpr int kStreamStages = 4;   // 64 KB ring, plus the prefix table: two workgroups per CU
+// 48 KB ring plus the 4 KB prefix table.  The four-wave kernel is compiled
+// for three workgroups per CU (at most 168 VGPRs: three waves per SIMD; 156
+// of gfx950's 160 KB of LDS), though the launch plan runs two per CU (see
+// kStreamWgsPerCU): ragged batch 909 us with a 4-stage ring and a budget of
+// two, 903-908 us with this ring and budget.
+constexpr int kStreamStages = 3;
 constexpr int kStreamMaxB = 1024;  // sequences whose stage prefix fits the LDS table
 constexpr int kRunStages = 128;    // stages covered by one page window (256 pages)
 
@@ -51,8 +56,13 @@ __device__ __forceinline__ int pick4(const int (&v)[4], int k) {
   return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
 }
 
+// Workgroups per compute unit each variant's register budget is compiled for.
+__host__ __device__ constexpr int stream_wgs_per_cu(int RB, int NR) {
+  return RB == 1 && NR == 4 ? 3 : RB == 1 ? 2 : 1;
+}
+
 template <int RB, int NR>
-__global__ __launch_bounds__(64 * NR) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
+__global__ __launch_bounds__(64 * NR) __attribute__((amdgpu_waves_per_eu(stream_wgs_per_cu(RB, NR))))
 void attn_partial_stream(AttnParams p, StreamParams sp) {
   constexpr int D = 128;
   constexpr int NC = D / 32;
@@ -283,20 +293,35 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
       VRow<D> vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) vv[e].v = *reinterpret_cast<const uint4*>(buf + (8 + e) * 1024);
+      // One softmax + PV code path for every stage, the masks (keys past the
+      // committed range, the in-block visibility) applied to the raw scores
+      // first.  With a single call site the accumulators stay in their
+      // registers from stage to stage; three specialised copies of the tile
+      // step made the compiler copy all 32 accumulator registers at every
+      // stage (234 -> 169 VGPRs, about 210 -> 130 VALU instructions per
+      // full stage; ragged batch 932 -> 909 us).
+      float x[RB][8];
+      tile_scores<D, RB>(qf, kf, x);
       if (i < ncs) {
         const int nk = L - 32 * i;
-        if (nk >= 32) {
-          mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [](int, int) { return true; });
-        } else {
-          mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st,
-                           [&](int, int e) { return pv_key(qd, e) < nk; });
+        if (nk < 32) {
+#pragma unroll
+          for (int k = 0; k < RB; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (pv_key(qd, e) >= nk) x[k][e] = neg_inf();
         }
       } else {
         const int j0 = 32 * (i - ncs);
-        mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [&](int k, int e) {
-          return ((vrow[k] >> (j0 + pv_key(qd, e))) & 1ull) != 0ull;
-        });
+#pragma unroll
+        for (int k = 0; k < RB; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (((vrow[k] >> (j0 + pv_key(qd, e))) & 1ull) == 0ull) x[k][e] = neg_inf();
       }
+      bf16x8 pf[RB], pl[RB];
+      tile_softmax<D, RB>(x, p.scale_log2, st, pf, pl, [](int, int) { return true; });
+      tile_pv<D, RB>(pf, pl, vv, st);
     }
     wait_vmem_barrier<0>();  // every wave is done with the ring before the next run fills it
 

@@ -30,10 +30,14 @@ constexpr int kMaxSplit = 2048;
 
 enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3, kMfmaNested = 4 };
 
-// Stream kernel: persistent grid sized for gfx950's 256 CUs (two workgroups
-// per CU at one row tile per wave, one at two) and rounded down to a multiple
-// of Hkv, each workgroup streaming at least kMinStreamStages stages.
+// Stream kernel: persistent grid of two workgroups per compute unit of
+// gfx950's 256, rounded down to a multiple of Hkv, each workgroup streaming
+// at least kMinStreamStages stages.  Two per CU with every CU equally loaded
+// is what the ragged batch measured fastest (512 workgroups 908 us; 768,
+// three per CU, 968 us: more page streams open at once; 576 or 640, some CUs
+// holding a third workgroup of equal length, 1131 and 1054 us; 384, 1022 us).
 constexpr int kCUs = 256;
+constexpr int kStreamWgsPerCU = 2;
 constexpr long kMinStreamStages = 2;
 // A handful of sequences is balanced by the split plan already, and the
 // stream kernel's per-workgroup set-up would dominate their short ranges.
@@ -153,7 +157,7 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
     if (upper < (1L << 30) && s.Hkv <= 65535) {
       pl.kernel = kMfmaStream;
       // G = Hkv * Gh: each KV head's list is cut into Gh ranges
-      const long slots = (long)kCUs * (pl.RB == 1 ? 2 : 1);
+      const long slots = (long)kCUs * kStreamWgsPerCU;
       const long per = s.split_tokens > 0 ? s.split_tokens / 32 : kMinStreamStages;
       const long upper_h = upper / s.Hkv;
       long Gh = (upper_h + per - 1) / per;
