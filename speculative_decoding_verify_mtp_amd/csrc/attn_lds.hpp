@@ -293,36 +293,51 @@ void attn_partial_lds(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) vv[e].v = *reinterpret_cast<const uint4*>(buf + (8 + e) * 1024);
 
+    // One softmax + PV code path for every stage (masks applied to the raw
+    // scores first) reached from one loop: specialised copies of the tile
+    // step made the compiler copy every accumulator register at each stage.
+    float x[RB][8];
+    tile_scores<D, RB>(qf, kf, x);
     if (s < ncs) {
       const int nk = end - (start + 32 * s);
-      if (nk >= 32) {
-        mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [](int, int) { return true; });
-      } else {
-        mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st,
-                         [&](int, int e) { return pv_key(qd, e) < nk; });
+      if (nk < 32) {
+#pragma unroll
+        for (int k = 0; k < RB; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (pv_key(qd, e) >= nk) x[k][e] = neg_inf();
       }
     } else {
       const int j0 = 32 * (s - ncs);
-      mfma_tile<D, RB>(qf, kf, vv, p.scale_log2, st, [&](int k, int e) {
-        return ((vrow[k] >> (j0 + pv_key(qd, e))) & 1ull) != 0ull;
-      });
+#pragma unroll
+      for (int k = 0; k < RB; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (((vrow[k] >> (j0 + pv_key(qd, e))) & 1ull) == 0ull) x[k][e] = neg_inf();
     }
+    bf16x8 pf[RB], pl[RB];
+    tile_softmax<D, RB>(x, p.scale_log2, st, pf, pl, [](int, int) { return true; });
+    tile_pv<D, RB>(pf, pl, vv, st);
   };
 
-  if (KS > 1 && nst <= kLdsStages) {
-    // every stage in the ring at once: one wait, one barrier, then each
-    // slice reduces its own stages
+  // Every stage in the ring at once (key slices, short splits): one wait, one
+  // barrier, then each slice reduces its own stages.  Otherwise a pipeline of
+  // kLdsStages - 1 stages in flight, slice ks reducing stages ks, ks + KS, ...
+  const bool at_once = KS > 1 && nst <= kLdsStages;
+  if (at_once) {
     for (int s = 0; s < nst; ++s) issue(s);
     wait_vmem_barrier<0>();
-    for (int s = ks; s < nst; s += KS) compute(s);
   } else {
     for (int s = 0; s < kLdsStages - 1 && s < nst; ++s) issue(s);
-    for (int s = 0; s < nst; ++s) {
+  }
+  for (int s = at_once ? ks : 0; s < nst; s += at_once ? KS : 1) {
+    if (!at_once) {
       const int after = min(kLdsStages - 2, nst - 1 - s);
       wait_stage_barrier<IPW>(after);
       if (s + kLdsStages - 1 < nst) issue(s + kLdsStages - 1);
-      if (s % KS == ks) compute(s);
+      if (s % KS != ks) continue;
     }
+    compute(s);
   }
 
   if constexpr (KS > 1) {
