@@ -73,18 +73,18 @@ __device__ __forceinline__ void wait_code_stage_barrier(int n) {
 // skv / svv: the raw scales of the lane's keys pv_key(q, 0..7); sl2 = the
 // softmax scale * log2(e) / 16 (so x * sl2 is the log2-domain score);
 // P' = p * s_v (sixteen times p * s_v / 16: the 1/16 is applied with the
-// offset at the end).  kMask: keys past nk are masked (selected, never
-// multiplied: their scales are arbitrary).
-template <int RB, bool kMask>
+// offset at the end).  Keys past nk (the last stage of a split) are masked
+// by selection and their V scales zeroed (a slot never written holds
+// arbitrary scales; p = 0 must not meet a NaN).  One code path for full and partial stages: with a specialised
+// copy for each, the compiler copied every accumulator register per stage.
+template <int RB>
 __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf16x8 (&kf)[2][4],
-                                            const float (&skv)[8], const float (&svv)[8],
+                                            const float (&skv)[8], float (&svv)[8],
                                             const float (&nqs)[RB], float sl2, int nk,
                                             MfmaState<128, RB>& st, float (&lp)[RB],
                                             bf16x8 (&pf)[RB], bf16x8 (&pl)[RB]) {
   const int qd = (threadIdx.x & 63) >> 4;
-  bool vis[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) vis[e] = !kMask || pv_key(qd, e) < nk;
+  float x[RB][8];
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -93,19 +93,26 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][m], qf[k][m], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][m], qf[k][m], s1, 0, 0, 0);
     }
-    float x[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[e] = skv[e] * (s0[e] + nqs[k]);
-      x[4 + e] = skv[4 + e] * (s1[e] + nqs[k]);
+      x[k][e] = skv[e] * (s0[e] + nqs[k]);
+      x[k][4 + e] = skv[4 + e] * (s1[e] + nqs[k]);
     }
-    if constexpr (kMask) {
+  }
+  if (nk < 32) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (!vis[e]) x[e] = neg_inf();
+    for (int e = 0; e < 8; ++e) {
+      if (pv_key(qd, e) >= nk) {
+        svv[e] = 0.f;
+#pragma unroll
+        for (int k = 0; k < RB; ++k) x[k][e] = neg_inf();
+      }
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  }
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    float mx = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
+                     fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
     mx = rows4_max(mx);
     mx *= sl2;
     const float mold = st.m[k];
@@ -115,9 +122,9 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
     __bf16 ph[8], plo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(fmaf(x[e], sl2, -muse));
+      const float pe = fast_exp2(fmaf(x[k][e], sl2, -muse));
       sum += pe;
-      const float pv = vis[e] ? pe * svv[e] : 0.f;
+      const float pv = pe * svv[e];
       sump += pv;
       ph[e] = (__bf16)pv;
       plo[e] = (__bf16)(pv - (float)ph[e]);
@@ -346,34 +353,15 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
       const float4 sk1 = *reinterpret_cast<const float4*>(code + 8192 + 64 + 16 * qd);
       const float4 sv0 = *reinterpret_cast<const float4*>(code + 8192 + 128 + 16 * qd);
       const float4 sv1 = *reinterpret_cast<const float4*>(code + 8192 + 192 + 16 * qd);
-      const float skv[8] = {sk0.x, sk0.y, sk0.z, sk0.w, sk1.x, sk1.y, sk1.z, sk1.w};
-      const float svv[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
+      float skv[8] = {sk0.x, sk0.y, sk0.z, sk0.w, sk1.x, sk1.y, sk1.z, sk1.w};
+      float svv[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
       const int nk = end - (start + 32 * s);
       bf16x8 pf[RB], pl[RB];
-      if (nk >= 32)
-        nest_scores<RB, false>(qf, kf, skv, svv, nqs, sl2, nk, st, lp, pf, pl);
-      else
-        nest_scores<RB, true>(qf, kf, skv, svv, nqs, sl2, nk, st, lp, pf, pl);
+      nest_scores<RB>(qf, kf, skv, svv, nqs, sl2, nk, st, lp, pf, pl);
       VRow<D> vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) vv[e].v = vraw[e];
-#define MTPV_NEST_LDS_PV(T)                                                                \
-  {                                                                                        \
-    const bf16x8 a = pack_v_operand<D, (T)>(vv);                                           \
-    _Pragma("unroll") for (int k = 0; k < RB; ++k) {                                       \
-      st.acc[k][(T)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[k], st.acc[k][(T)], 0, 0, 0); \
-      st.acc[k][(T)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[k], st.acc[k][(T)], 0, 0, 0); \
-    }                                                                                      \
-  }
-      MTPV_NEST_LDS_PV(0)
-      MTPV_NEST_LDS_PV(1)
-      MTPV_NEST_LDS_PV(2)
-      MTPV_NEST_LDS_PV(3)
-      MTPV_NEST_LDS_PV(4)
-      MTPV_NEST_LDS_PV(5)
-      MTPV_NEST_LDS_PV(6)
-      MTPV_NEST_LDS_PV(7)
-#undef MTPV_NEST_LDS_PV
+      tile_pv<D, RB>(pf, pl, vv, st);
     }
   }
 
