@@ -100,6 +100,39 @@ struct MfmaState {
 // relative to the reference stay below 2^8, far from fp32 overflow.
 constexpr float kRescaleSlack = 8.f;
 
+// Largest of eight scores.  IEEE maximum (NaN-propagating) maps to gfx950's
+// three-input v_maximum3_f32 and, unlike fmaxf, needs no quieting of the
+// MFMA results first; the masked scores are -inf, never NaN.  (Used by the
+// nested-cache kernel: 1110 -> 1089 us with this and split_bf16_hi_lo on the
+// ragged batch; the bf16 stream kernel measured 915 -> 928 us with them and
+// keeps fmaxf and per-value conversions.)
+__device__ __forceinline__ float max8(const float (&x)[8]) {
+  const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), x[2]);
+  const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3], x[4]), x[5]);
+  const float c = __builtin_elementwise_maximum(x[6], x[7]);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// p = hi + lo with hi = bf16(p) (round to nearest even) and lo = bf16(p - hi)
+// (p - hi is exact in fp32), eight values packed as two bf16x8 MFMA operands.
+// Two values per conversion; hi comes back to fp32 by a shift or a mask.
+__device__ __forceinline__ void split_bf16_hi_lo(const float (&p)[8], bf16x8& hi, bf16x8& lo) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  unsigned hw[4], lw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x2 h2 = {(__bf16)p[2 * j], (__bf16)p[2 * j + 1]};
+    unsigned u;
+    __builtin_memcpy(&u, &h2, 4);
+    hw[j] = u;
+    const float h0 = __uint_as_float(u << 16), h1 = __uint_as_float(u & 0xffff0000u);
+    const bf16x2 l2 = {(__bf16)(p[2 * j] - h0), (__bf16)(p[2 * j + 1] - h1)};
+    __builtin_memcpy(&lw[j], &l2, 4);
+  }
+  __builtin_memcpy(&hi, hw, 16);
+  __builtin_memcpy(&lo, lw, 16);
+}
+
 // Raw scores of one 32-key tile for the RB row tiles: x[k][e] = q . k of
 // this lane's row of tile k and its e-th key (keys {4q..4q+3} of the first
 // 16-key half, then the same of the second), unscaled.

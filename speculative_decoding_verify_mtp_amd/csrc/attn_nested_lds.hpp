@@ -111,24 +111,20 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
   }
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
-    float mx = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
-                     fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
+    float mx = max8(x[k]);
     mx = rows4_max(mx);
     mx *= sl2;
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
     const float muse = mref == neg_inf() ? 0.f : mref;
-    float sum = 0.f, sump = 0.f;
-    __bf16 ph[8], plo[8];
+    float pe[8], pv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(fmaf(x[k][e], sl2, -muse));
-      sum += pe;
-      const float pv = pe * svv[e];
-      sump += pv;
-      ph[e] = (__bf16)pv;
-      plo[e] = (__bf16)(pv - (float)ph[e]);
+      pe[e] = fast_exp2(fmaf(x[k][e], sl2, -muse));
+      pv[e] = pe[e] * svv[e];
     }
+    const float sum = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+    const float sump = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     if (__ballot(mref != mold) != 0ull) {
       const float alpha = fast_exp2(mold - muse);
       st.l[k] *= alpha;
@@ -139,8 +135,7 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
     st.l[k] += sum;
     lp[k] += sump;
     st.m[k] = mref;
-    __builtin_memcpy(&pf[k], ph, sizeof(bf16x8));
-    __builtin_memcpy(&pl[k], plo, sizeof(bf16x8));
+    split_bf16_hi_lo(pv, pf[k], pl[k]);
   }
 }
 
