@@ -133,10 +133,10 @@ def write_traffic(workload: str, ctr_dir: str) -> int:
         "bytes_per_launch": int(fetch * 1024 * ff + write * 1024 * fw),
         "commands": [
             f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d {ctr_dir}/{t}_{c} -o run "
-            f"-- python bench.py " + (f"--workload {workload} {steps} --no-cpu-baseline"
+            f"-- python3 bench.py " + (f"--workload {workload} {steps} --no-cpu-baseline"
                                       if t == workload else "--copy-calibration 512")
             for t in (workload, "copy") for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
-            f"python bench.py --write-traffic {workload} --ctr-dir {ctr_dir}"],
+            f"python3 bench.py --write-traffic {workload} --ctr-dir {ctr_dir}"],
         "note": "medians over dispatches of the partial kernel; the copy kernel moves 512 MB "
                 "each way, so factor = 500000 KiB / counter reading",
     }
