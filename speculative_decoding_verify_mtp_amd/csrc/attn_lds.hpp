@@ -122,7 +122,11 @@ void attn_partial_lds(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char ring[kLdsStages * kStageBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;  // 0 .. NW - 1
+  // wave-uniform, so the issue path computes page addresses in scalar registers
+  // (bitnet2b_chain partial 9.18 -> 9.01 us, llama3_8b_tree 19.9 -> 19.7 us;
+  // the stream kernel measured 925 -> 934 us with the same change and keeps
+  // the vector form)
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0 .. NW - 1
   const int tg = wv % NR;           // row-tile group
   const int ks = wv / NR;           // key slice
   const int c = lane & 15;
