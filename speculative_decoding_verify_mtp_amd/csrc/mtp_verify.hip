@@ -131,6 +131,9 @@ mtp_status build_attn(const mtp_shape* shape, const void* q, const void* k_cache
   a.sp.nts = pl.nts;
   a.sp.nseg = pl.nseg;
   a.sp.rows_block = pl.rows_block;
+  a.sp.h1 = pl.h1;
+  a.sp.w_num = kFirstRoundNum;
+  a.sp.w_den = kFirstRoundDen;
   return MTP_OK;
 }
 

@@ -39,6 +39,10 @@ enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3, kMfmaNe
 constexpr int kCUs = 256;
 constexpr int kStreamWgsPerCU = 2;
 constexpr long kMinStreamStages = 2;
+// Length of a first-dispatch-round range relative to the others (two
+// workgroups per CU; ragged batch: equal ranges 900 us, first-round share of
+// the list 0.53 / 0.55 / 0.57 / 0.59: 882 / 872 / 878 / 908 us).
+constexpr int kFirstRoundNum = 5, kFirstRoundDen = 4;
 // A handful of sequences is balanced by the split plan already, and the
 // stream kernel's per-workgroup set-up would dominate their short ranges.
 constexpr int kStreamMinB = 8;
@@ -54,6 +58,7 @@ struct Plan {
   int S;           // committed tokens per split
   int max_splits;  // splits of the longest context
   int G;           // stream kernel: workgroups
+  int h1;          // stream kernel: ranges per head in the first dispatch round (0: equal ranges)
   int nts, nseg, rows_block;
   size_t acc_bytes, ml_offset, ml_bytes, seg_offset, seg_bytes;
 };
@@ -147,6 +152,7 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
   }
   pl.max_splits = s.max_ctx_len > 0 ? (s.max_ctx_len + pl.S - 1) / pl.S : 1;
   pl.G = 0;
+  pl.h1 = 0;
   pl.nseg = s.Hkv * pl.nRB;
   pl.rows_block = 16 * pl.NR * pl.RB;
   size_t rows = (size_t)s.B * pl.max_splits * s.Hkv * pl.R;
@@ -157,7 +163,8 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
     if (upper < (1L << 30) && s.Hkv <= 65535) {
       pl.kernel = kMfmaStream;
       // G = Hkv * Gh: each KV head's list is cut into Gh ranges
-      const long slots = (long)kCUs * kStreamWgsPerCU;
+      // (two row tiles per wave take a SIMD's registers: one workgroup per CU)
+      const long slots = (long)kCUs * (pl.RB == 1 ? kStreamWgsPerCU : 1);
       const long per = s.split_tokens > 0 ? s.split_tokens / 32 : kMinStreamStages;
       const long upper_h = upper / s.Hkv;
       long Gh = (upper_h + per - 1) / per;
@@ -165,6 +172,9 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
       if (s.split_tokens == 0 && Gh > slots_h) Gh = slots_h;
       const long max_h = 65535 / s.Hkv;
       pl.G = (int)((Gh < 1 ? 1 : (Gh > max_h ? max_h : Gh)) * s.Hkv);
+      // Two workgroups per CU: the G - 256 workgroups past the first round
+      // share CUs with first-round ones, whose ranges are made longer.
+      if (s.split_tokens == 0 && pl.RB == 1 && pl.G > kCUs) pl.h1 = kCUs / s.Hkv;
       rows = ((size_t)pl.G + (size_t)s.B * pl.nseg) * pl.rows_block;
     }
   }

@@ -134,6 +134,23 @@ def test_stream_ranges_per_kv_head(wl, split):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"{wl.name} split {split}")
 
 
+# Two workgroups per CU and at least 32 stages per range: the ranges of the
+# first dispatch round are longer than the rest (Hkv = 8: 32 + 32 ranges per
+# head; Hkv = 5: 51 + 51).
+STREAM_WEIGHTED = [
+    W_("stream_weighted_hkv8", B=20, Hq=32, Hkv=8, W=16, ctx_lo=3500, ctx_hi=5500, masks="mixed"),
+    W_("stream_weighted_hkv5", B=24, Hq=20, Hkv=5, W=8, ctx_lo=5000, ctx_hi=6000, masks="chain"),
+]
+
+
+@pytest.mark.parametrize("wl", STREAM_WEIGHTED, ids=[w.name for w in STREAM_WEIGHTED])
+def test_stream_weighted_ranges(wl):
+    inp = gpu_inputs(wl, 19)
+    out, lse = run_attn(inp)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
+
+
 PHASES = [
     W_("phase_split", B=3, Hq=20, Hkv=5, W=8, ctx_lo=100, ctx_hi=900),
     W_("phase_stream", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=900, masks="mixed"),
