@@ -134,7 +134,7 @@ void attn_partial_lds(AttnParams p) {
   const int b = blockIdx.y;
   const Item it = decode_item_xcd(blockIdx.x, gridDim.x, p);
   if (it.split >= p.max_splits) return;  // uniform over the workgroup
-  const int start = it.split * p.S;
+  const int start = split_start(p, it.split);
 
   // Loads that do not depend on the context length go out together with it:
   // the split's page indices (bounded by the block table) and Q.
@@ -167,9 +167,9 @@ void attn_partial_lds(AttnParams p) {
   const int mid = lane_mask_id(p, b, lane);
   const int L = p.ctx_lens[b];
   if (L < 0 || L > p.max_ctx) return;
-  const int ns = num_splits(L, p.S);
+  const int ns = num_splits(p, L);
   if (it.split >= ns) return;
-  const int end = min(L, start + p.S);
+  const int end = min(L, split_start(p, it.split + 1));
   const bool last = it.split == ns - 1;
 
   const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache) + (size_t)it.kvh * D;

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
   const int b = blockIdx.y;
   const Item it = decode_item(blockIdx.x * 4 + (threadIdx.x >> 6), p);
   if (it.split >= p.max_splits) return;
-  const int start = it.split * p.S;
+  const int start = split_start(p, it.split);
 
   // Loads that do not depend on the context length go out together with it:
   // the split's page indices (held in two registers per lane: lane i has
@@ -300,9 +300,9 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
   const int mid = lane_mask_id(p, b, lane);
   const int L = p.ctx_lens[b];
   if (L < 0 || L > p.max_ctx) return;  // reported by the combine
-  const int ns = num_splits(L, p.S);
+  const int ns = num_splits(p, L);
   if (it.split >= ns) return;
-  const int end = min(L, start + p.S);
+  const int end = min(L, split_start(p, it.split + 1));
   const bool last = it.split == ns - 1;
 
   MfmaState<D, RB> st;

@@ -159,7 +159,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
   const int b = blockIdx.y;
   const Item it = decode_item_xcd(blockIdx.x, gridDim.x, p);
   if (it.split >= p.max_splits) return;  // uniform over the workgroup
-  const int start = it.split * p.S;
+  const int start = split_start(p, it.split);
 
   const int32_t* btrow = p.block_table + (size_t)b * p.max_pages + start / kPage;
   const int pavail = p.max_pages - start / kPage;
@@ -198,9 +198,9 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
   const int mid = lane_mask_id(p, b, lane);
   const int L = p.ctx_lens[b];
   if (L < 0 || L > p.max_ctx) return;
-  const int ns = num_splits(L, p.S);
+  const int ns = num_splits(p, L);
   if (it.split >= ns) return;
-  const int end = min(L, start + p.S);
+  const int end = min(L, split_start(p, it.split + 1));
   const bool last = it.split == ns - 1;
   const int npg = (end - start + kPage - 1) / kPage;
   bool bad = (lane < npg && (unsigned)pr0 >= (unsigned)p.num_pages) ||

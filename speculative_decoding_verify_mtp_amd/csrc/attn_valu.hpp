@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
   const int b = blockIdx.y;
   const Item it = decode_item(blockIdx.x * 4 + (threadIdx.x >> 6), p);
   if (it.split >= p.max_splits) return;
-  const int start = it.split * p.S;
+  const int start = split_start(p, it.split);
   // Loads that do not depend on the context length go out together with it:
   // the split's page indices (lane i holding entries i and 64 + i; a split
   // spans at most 128 pages; bounded by the block table, not by the
@@ -93,9 +93,9 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
 
   const int L = p.ctx_lens[b];
   if (L < 0 || L > p.max_ctx) return;
-  const int ns = num_splits(L, p.S);
+  const int ns = num_splits(p, L);
   if (it.split >= ns) return;
-  const int end = min(L, start + p.S);
+  const int end = min(L, split_start(p, it.split + 1));
   const bool last = it.split == ns - 1;
 
   // In-block visibility rows of this item's rows (last split only).

@@ -68,7 +68,7 @@ __device__ __forceinline__ void combine_rows(const AttnParams& p, unsigned block
     if (p.lse != nullptr && lane == 0) p.lse[row] = qnan();
     return;
   }
-  const int ns = num_splits(L, p.S);
+  const int ns = num_splits(p, L);
   const int nfast = ns < 4 * kBatch ? ns : 4 * kBatch;
 
   const bool have = lane < ns;
@@ -228,7 +228,7 @@ __device__ __forceinline__ void combine_rows_grouped(const AttnParams& p, const 
       continue;
     }
 
-    if constexpr (!kStream) ns = num_splits(L, p.S);
+    if constexpr (!kStream) ns = num_splits(p, L);
     float M = neg_inf(), den = 0.f;
     float a[VPL];
 #pragma unroll

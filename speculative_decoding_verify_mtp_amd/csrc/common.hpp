@@ -159,8 +159,9 @@ struct AttnParams {
   float* lse;       // [B, W, Hq] or null
   int B, W, Hq, Hkv, g, R;
   int nRB;         // row blocks per (sequence, KV head)
-  int S;           // committed tokens per split (multiple of 32)
-  int max_splits;  // max(1, ceil(max_ctx / S))
+  int S;           // committed tokens per split (multiple of 32) past the first n1 splits
+  int n1, S1;      // splits 0 .. n1 - 1 hold S1 tokens each (n1 = 0: every split holds S)
+  int max_splits;  // splits of max_ctx
   int max_pages, num_pages, max_ctx, lookback;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -209,7 +210,19 @@ __device__ __forceinline__ Item decode_item_xcd(int item, int n_items, const Att
   return it;
 }
 
-__device__ __forceinline__ int num_splits(int L, int S) { return L > 0 ? (L + S - 1) / S : 1; }
+// Split geometry of the per-split kernels: splits 0 .. n1 - 1 hold S1
+// committed tokens, the later ones S; a context of L tokens has
+// num_splits(...) splits (at least one: the block's own rows).
+__host__ __device__ inline int split_start(int s, int S, int n1, int S1) {
+  return s <= n1 ? s * S1 : n1 * S1 + (s - n1) * S;
+}
+__host__ __device__ inline int num_splits(int L, int S, int n1, int S1) {
+  if (L <= 0) return 1;
+  const int head = n1 * S1;
+  return L <= head ? (L + S1 - 1) / S1 : n1 + (L - head + S - 1) / S;
+}
+__device__ __forceinline__ int split_start(const AttnParams& p, int s) { return split_start(s, p.S, p.n1, p.S1); }
+__device__ __forceinline__ int num_splits(const AttnParams& p, int L) { return num_splits(L, p.S, p.n1, p.S1); }
 
 // Lane's mask id of sequence b (0 for lanes past the block).
 __device__ __forceinline__ int lane_mask_id(const AttnParams& p, int b, int lane) {

@@ -120,6 +120,8 @@ mtp_status build_attn(const mtp_shape* shape, const void* q, const void* k_cache
   p.R = pl.R;
   p.nRB = pl.nRB;
   p.S = pl.S;
+  p.n1 = pl.n1;
+  p.S1 = pl.S1;
   p.max_splits = pl.max_splits;
   p.max_pages = s.max_pages_per_seq;
   p.num_pages = s.num_pages;

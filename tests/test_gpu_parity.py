@@ -151,6 +151,29 @@ def test_stream_weighted_ranges(wl):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
 
 
+# One sequence, 128 rows per KV head (two row blocks of 64), 288 to 512
+# items: the splits of the first dispatch round hold 288 tokens, the rest
+# 224.  The last case bounds the context at 8192 tokens but holds 3000, so it
+# ends inside the long splits.
+WEIGHTED_SPLITS = [
+    (W_("wsplit_6000", B=1, Hq=32, Hkv=8, W=32, ctx_lo=6000, ctx_hi=6000, masks="tree"), None),
+    (W_("wsplit_5000", B=1, Hq=32, Hkv=8, W=32, ctx_lo=5000, ctx_hi=5000, masks="chain"), None),
+    (W_("wsplit_bound", B=1, Hq=32, Hkv=8, W=32, ctx_lo=3000, ctx_hi=3000, masks="tree"), 8192),
+]
+
+
+@pytest.mark.parametrize("wl,bound", WEIGHTED_SPLITS, ids=[w.name for w, _ in WEIGHTED_SPLITS])
+def test_single_sequence_weighted_splits(wl, bound):
+    inp = gpu_inputs(wl, 23)
+    if bound is not None:  # a table wide enough for the bound (unmapped entries past the context)
+        bt = inp["block_table"]
+        pad = torch.full((bt.shape[0], bound // 16 - bt.shape[1]), -1, dtype=bt.dtype, device=bt.device)
+        inp["block_table"] = torch.cat([bt, pad], dim=1).contiguous()
+    out, lse = run_attn(inp, max_ctx_len=bound)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
+
+
 PHASES = [
     W_("phase_split", B=3, Hq=20, Hkv=5, W=8, ctx_lo=100, ctx_hi=900),
     W_("phase_stream", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=900, masks="mixed"),
