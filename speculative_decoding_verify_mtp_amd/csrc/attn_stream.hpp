@@ -88,6 +88,35 @@ __device__ __forceinline__ int pick4(const int (&v)[4], int k) {
   return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
 }
 
+// Stage prefix over the sequences of one head's list: s_pref[b] = stages of
+// sequences < b (s_pref[B] = the list's length), each sequence ceil(L / 32)
+// committed and nts in-block stages per row block; a sequence whose context
+// lies outside [0, max_ctx] has none.  Wave 0 computes it; all threads wait.
+__device__ __forceinline__ void stream_prefix(const AttnParams& p, int nts, int* s_pref) {
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) == 0) {
+    int run = 0;
+    for (int b0 = 0; b0 < p.B; b0 += kWave) {
+      const int bb = b0 + lane;
+      int n = 0;
+      if (bb < p.B) {
+        const int L = p.ctx_lens[bb];
+        if (L >= 0 && L <= p.max_ctx) n = ((L + 31) / 32 + nts) * p.nRB;
+      }
+      int x = n;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (bb < p.B) s_pref[bb + 1] = run + x;
+      run += __shfl(x, 63);
+    }
+    if (lane == 0) s_pref[0] = 0;
+  }
+  __syncthreads();
+}
+
 // Workgroups per compute unit each variant's register budget is compiled for.
 __host__ __device__ constexpr int stream_wgs_per_cu(int RB, int NR) {
   return RB == 1 && NR == 4 ? 3 : RB == 1 ? 2 : 1;
@@ -111,28 +140,7 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
   const int c = lane & 15;
   const int qd = lane >> 4;
 
-  // ---- stage prefix over sequences of one head's list: s_pref[b] = stages of sequences < b
-  if (wv == 0) {
-    int run = 0;
-    for (int b0 = 0; b0 < p.B; b0 += kWave) {
-      const int bb = b0 + lane;
-      int n = 0;
-      if (bb < p.B) {
-        const int L = p.ctx_lens[bb];
-        if (L >= 0 && L <= p.max_ctx) n = ((L + 31) / 32 + sp.nts) * p.nRB;
-      }
-      int x = n;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
-      if (bb < p.B) s_pref[bb + 1] = run + x;
-      run += __shfl(x, 63);
-    }
-    if (lane == 0) s_pref[0] = 0;
-  }
-  __syncthreads();
+  stream_prefix(p, sp.nts, s_pref);
   const int total = s_pref[p.B];
   const int Gh = G / p.Hkv;          // ranges per head (the host makes G a multiple of Hkv)
   const int gi = wg / p.Hkv;         // this workgroup's range

@@ -21,6 +21,7 @@
 #include "tree.hpp"
 #include "plan.hpp"
 #include "attn_nested_lds.hpp"
+#include "attn_nested_stream.hpp"
 #include "mtp_verify.h"
 
 namespace {
@@ -146,7 +147,13 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
   const StreamParams& sp = a.sp;
   const dim3 block(256);
   const long items = (long)pl.max_splits * p.Hkv * pl.nRB;
-  if (pl.kernel == kMfmaNested) {
+  if (pl.kernel == kMfmaNestedStream) {
+    const dim3 sgrid((unsigned)pl.G);
+    const dim3 sblock(64 * pl.NR);
+    if (pl.NR == 4) attn_partial_nested_stream<4><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+    else if (pl.NR == 2) attn_partial_nested_stream<2><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+    else attn_partial_nested_stream<1><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+  } else if (pl.kernel == kMfmaNested) {
     const dim3 wgrid((unsigned)items, (unsigned)B);
     const dim3 wblock(64 * pl.NR);
     if (pl.NR == 4) attn_partial_nested_lds<1, 4><<<wgrid, wblock, 0, strm>>>(p, *na);
@@ -187,7 +194,7 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
 // stream layout and for split layouts with few splits, one otherwise.
 // `finish`: the step's finish launch (grouped for the stream layout only).
 bool grouped_combine(const AttnParams& p, const Plan& pl, bool finish) {
-  return pl.kernel == kMfmaStream ||
+  return stream_layout(pl.kernel) ||
          (!finish && grouped_split_combine(pl.max_splits, (long)p.B * p.W * p.Hq));
 }
 int combine_rows_per_wave(const AttnParams& p, const Plan& pl, bool finish) {
@@ -233,7 +240,7 @@ int finish_combine_waves(const AttnParams& p, const Plan& pl) {
 
 void launch_combine(const Attn& a, int D, hipStream_t strm) {
   const dim3 cgrid(combine_blocks(a.p, a.pl, false, 4, 4L * kCUs)), block(256);
-  if (a.pl.kernel == kMfmaStream) attn_combine<128, true><<<cgrid, block, 0, strm>>>(a.p, a.sp);
+  if (stream_layout(a.pl.kernel)) attn_combine<128, true><<<cgrid, block, 0, strm>>>(a.p, a.sp);
   else if (D == 128) attn_combine<128, false><<<cgrid, block, 0, strm>>>(a.p, a.sp);
   else attn_combine<64, false><<<cgrid, block, 0, strm>>>(a.p, a.sp);
 }
@@ -428,7 +435,7 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
     const dim3 fgrid((unsigned)shape->B +
                      combine_blocks(a.p, a.pl, true, crows, finish_combine_cus(a.p, a.pl))),
         block(kAcceptThreads);
-    if (a.pl.kernel == kMfmaStream)
+    if (stream_layout(a.pl.kernel))
       finish_kernel<128, true><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);
     else if (shape->D == 128)
       finish_kernel<128, false><<<fgrid, block, 0, strm>>>(a.p, a.sp, ap, cp, crows);

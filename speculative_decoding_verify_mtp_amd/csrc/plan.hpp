@@ -28,7 +28,10 @@ constexpr long kTargetWaves = 2048;
 constexpr int kMinSplit = 32;  // one 32-key stage: short contexts are latency-bound
 constexpr int kMaxSplit = 2048;
 
-enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3, kMfmaNested = 4 };
+enum Kernel { kValu = 0, kMfmaDirect = 1, kMfmaLds = 2, kMfmaStream = 3, kMfmaNested = 4, kMfmaNestedStream = 5 };
+
+// Kernels that write the stream layout (pieces per range and segment, a segment table).
+inline bool stream_layout(int kernel) { return kernel == kMfmaStream || kernel == kMfmaNestedStream; }
 
 // Stream kernel: persistent grid of two workgroups per compute unit of
 // gfx950's 256, rounded down to a multiple of Hkv, each workgroup streaming
@@ -137,7 +140,8 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
     pl.S = S < kMinSplit ? kMinSplit : (S > kMaxSplit ? kMaxSplit : S);
   }
   pl.nts = (s.W + 31) / 32;
-  const bool stream_shape = pl.kernel == kMfmaLds && s.B >= kStreamMinB && s.B <= kStreamMaxB;
+  const bool stream_shape = (pl.kernel == kMfmaLds || pl.kernel == kMfmaNested) && s.B >= kStreamMinB &&
+                            s.B <= kStreamMaxB;
   // Per-split LDS kernel with one or two row tiles per workgroup: two key
   // slices (each wave reduces half of the stages) when every stage of a split
   // fits the ring.  The automatic split then also grows, within the ring, until
@@ -160,11 +164,25 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
   pl.rows_block = 16 * pl.NR * pl.RB;
   size_t rows = (size_t)s.B * pl.max_splits * s.Hkv * pl.R;
   if (stream_shape) {
+    // The nested stream kernel runs one row tile per wave: row blocks of at
+    // most 64 rows, a segment each.
+    const bool nested_rb1 = pl.kernel == kMfmaNested && pl.RB == 2;
+    const int nrb = nested_rb1 ? (tiles + pl.NR - 1) / pl.NR : pl.nRB;
     // stage count bound from max_ctx_len; the device splits the true count
     const long seg_stages = (long)(s.max_ctx_len + 31) / 32 + pl.nts;
-    const long upper = (long)s.B * pl.nseg * seg_stages;
+    const long upper = (long)s.B * s.Hkv * nrb * seg_stages;
     if (upper < (1L << 30) && s.Hkv <= 65535) {
-      pl.kernel = kMfmaStream;
+      if (pl.kernel == kMfmaNested) {
+        pl.kernel = kMfmaNestedStream;
+        if (nested_rb1) {
+          pl.RB = 1;
+          pl.nRB = nrb;
+          pl.nseg = s.Hkv * pl.nRB;
+          pl.rows_block = 16 * pl.NR;
+        }
+      } else {
+        pl.kernel = kMfmaStream;
+      }
       // G = Hkv * Gh: each KV head's list is cut into Gh ranges
       // (two row tiles per wave take a SIMD's registers: one workgroup per CU)
       const long slots = (long)kCUs * (pl.RB == 1 ? kStreamWgsPerCU : 1);
@@ -217,7 +235,7 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
   pl.ml_offset = (pl.acc_bytes + 255) & ~(size_t)255;
   pl.ml_bytes = rows * 2 * sizeof(float);
   pl.seg_offset = (pl.ml_offset + pl.ml_bytes + 255) & ~(size_t)255;
-  pl.seg_bytes = pl.kernel == kMfmaStream ? (size_t)s.B * pl.nseg * 2 * sizeof(int) : 0;
+  pl.seg_bytes = stream_layout(pl.kernel) ? (size_t)s.B * pl.nseg * 2 * sizeof(int) : 0;
   return pl;
 }
 

@@ -133,6 +133,53 @@ def test_nested_attention_matches_oracle(wl, recent):
     assert lib.device_status(clear=True) == 0
 
 
+# Eight or more sequences: the nested stream-K kernel (ranges of the list of
+# 32-key stages of every segment; pieces per range and segment).
+NESTED_STREAM = [
+    W_("ns_mixed", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=900, masks="mixed"),
+    # 128 rows per KV head: two row blocks of 64 (two segments per sequence and head)
+    W_("ns_rows128", B=8, Hq=32, Hkv=8, W=32, ctx_lo=40, ctx_hi=700, masks="tree"),
+    W_("ns_hkv5", B=9, Hq=20, Hkv=5, W=8, ctx_lo=0, ctx_hi=1100, masks="chain"),
+    W_("ns_r16", B=10, Hq=8, Hkv=4, W=8, ctx_lo=15, ctx_hi=300, masks="mixed"),
+    # 33 rows per sequence and head (a padded tile), segments with lookback 1
+    W_("ns_r33", B=8, Hq=3, Hkv=1, W=11, ctx_lo=0, ctx_hi=500, masks="segment", seg_lookback=1),
+]
+
+
+@pytest.mark.parametrize("recent", [-1, 0, 37])
+@pytest.mark.parametrize("wl", NESTED_STREAM, ids=[w.name for w in NESTED_STREAM])
+def test_nested_stream_attention_matches_oracle(wl, recent):
+    inp = gpu_inputs(wl, 14)
+    kv = quantized(inp)
+    kp, vp = oracle_planes(inp)
+    out, lse = lib.verify_attn_nested(inp["q"], kv, inp["block_table"], inp["ctx_lens"],
+                                      inp["k_new"], inp["v_new"], inp["mask_kind"],
+                                      inp["mask_ids"], kv8_recent=recent,
+                                      max_ctx_len=int(inp["host"]["ctx_lens"].max()),
+                                      scale=inp["scale"], seg_lookback=inp["seg_lookback"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_nested(inp, kp, vp, recent)
+    assert_attn_close(out, lse, ref_out, ref_lse, ATOL, RTOL, f"{wl.name} recent={recent}")
+    assert lib.device_status(clear=True) == 0
+
+
+@pytest.mark.parametrize("split", [32, 96, 1024])
+def test_nested_stream_work_split_does_not_change_the_result(split):
+    """Workgroups of 1, 3 or 32 stages: ranges start and end inside
+    committed stages and inside the in-block stage."""
+    wl = W_("ns_split", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=1500, masks="mixed")
+    inp = gpu_inputs(wl, 15)
+    kv = quantized(inp)
+    kp, vp = oracle_planes(inp)
+    out, lse = lib.verify_attn_nested(inp["q"], kv, inp["block_table"], inp["ctx_lens"],
+                                      inp["k_new"], inp["v_new"], inp["mask_kind"],
+                                      inp["mask_ids"], kv8_recent=600, scale=inp["scale"],
+                                      split_tokens=split)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_nested(inp, kp, vp, 600)
+    assert_attn_close(out, lse, ref_out, ref_lse, ATOL, RTOL, f"stream split={split}")
+
+
 @pytest.mark.parametrize("split", [32, 64, 2048])
 def test_nested_split_size_does_not_change_the_result(split):
     wl = W_("n_split", B=3, Hq=16, Hkv=4, W=8, ctx_lo=500, ctx_hi=1300, masks="mixed")
