@@ -13,6 +13,10 @@
 // segment part, when the part's committed stages are followed by in-block
 // stages or when the piece is written.  A segment's in-block stages (bf16
 // rows of the block) are read with direct loads.
+//
+// KV4 (every committed key read at 4 bits): only the base-plane images are
+// loaded and transcoded (4 code images per stage instead of 8; the
+// refinement code is the constant 0).
 #pragma once
 
 #include "attn_mfma.hpp"
@@ -23,14 +27,14 @@
 
 namespace mtpv {
 
-template <int NR>
+template <int NR, bool KV4>
 __global__ __launch_bounds__(64 * NR) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
   constexpr int D = 128;
   constexpr int RB = 1;
   constexpr int NC = D / 32;
   constexpr int NT = D / 16;
-  constexpr int CPW = 8 / NR;   // code images per wave per stage
+  constexpr int CPW = (KV4 ? 4 : 8) / NR;  // code images per wave per stage
   constexpr int PER = CPW + 1;  // loads per wave per stage (codes + scales)
   constexpr int IPW = 16 / NR;  // operand images transcoded per wave
   constexpr int SL = kWave / NR;
@@ -206,7 +210,10 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
       const bool any8 = min(t0 + 31, L - 1) >= kv8_from;
 #pragma unroll
       for (int k = 0; k < CPW; ++k) {
-        const int im = wv + NR * k;  // 0..7: kind = im / 2, half = im % 2
+        // image 0..7: kind = im / 2 (K base, K ref, V base, V ref), half = im % 2;
+        // KV4 loads images 0, 1, 4, 5
+        const int j = wv + NR * k;
+        const int im = KV4 ? ((j >> 1) << 2) | (j & 1) : j;
         const int kind = im >> 1, half = im & 1;
         const uint8_t* b2 = (kind & 2) ? vbase : kbase;
         const uint8_t* r2 = (kind & 2) ? vref : kref;
@@ -254,8 +261,11 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
           key = 16 * half + k16;
         }
         const unsigned bw = *reinterpret_cast<const unsigned*>(cb + off);
-        unsigned rw = *reinterpret_cast<const unsigned*>(cb + 2048 + off);
-        if (t0 + key < kv8_from) rw = kNestZeroRef;
+        unsigned rw = kNestZeroRef;
+        if constexpr (!KV4) {
+          rw = *reinterpret_cast<const unsigned*>(cb + 2048 + off);
+          if (t0 + key < kv8_from) rw = kNestZeroRef;
+        }
         unsigned ev, od;
         nest_bytes(bw, rw, ev, od);
         *reinterpret_cast<uint4*>(out + im * 1024) =

@@ -150,9 +150,15 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
   if (pl.kernel == kMfmaNestedStream) {
     const dim3 sgrid((unsigned)pl.G);
     const dim3 sblock(64 * pl.NR);
-    if (pl.NR == 4) attn_partial_nested_stream<4><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
-    else if (pl.NR == 2) attn_partial_nested_stream<2><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
-    else attn_partial_nested_stream<1><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+    if (na->kv8_recent == 0) {  // every committed key at 4 bits: base plane only
+      if (pl.NR == 4) attn_partial_nested_stream<4, true><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+      else if (pl.NR == 2) attn_partial_nested_stream<2, true><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+      else attn_partial_nested_stream<1, true><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+    } else {
+      if (pl.NR == 4) attn_partial_nested_stream<4, false><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+      else if (pl.NR == 2) attn_partial_nested_stream<2, false><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+      else attn_partial_nested_stream<1, false><<<sgrid, sblock, 0, strm>>>(p, sp, *na);
+    }
   } else if (pl.kernel == kMfmaNested) {
     const dim3 wgrid((unsigned)items, (unsigned)B);
     const dim3 wblock(64 * pl.NR);
