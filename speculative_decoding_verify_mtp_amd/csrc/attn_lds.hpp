@@ -31,6 +31,14 @@
 namespace mtpv {
 
 constexpr int kLdsStages = 5;  // 80 KB per workgroup: two workgroups fill gfx950's 160 KB
+// Stages in flight ahead of the one being reduced when a split streams
+// through the ring.  Fewer outstanding stages per workgroup keep the memory
+// queues short, so every workgroup's next stage arrives sooner: llama3_8b_tree
+// 18.5-19.0 -> 17.1-17.8 us with 2 instead of 4 (3: 17.8-18.2 us, 1:
+// 17.4 us); 4 sequences of 16000 tokens 67.0 -> 64.6 us; 2 of 30000 with
+// W = 32 95.4 -> 90.8 us.
+constexpr int kLdsAhead = 2;
+static_assert(kLdsAhead >= 1 && kLdsAhead <= kLdsStages - 1, "ring slots refilled after their last read");
 constexpr int kStageBytes = 16 * 1024;
 constexpr int kMaxSplitPages = 128;  // page indices of a split held in two registers per lane
 
@@ -326,19 +334,19 @@ void attn_partial_lds(AttnParams p) {
 
   // Every stage in the ring at once (key slices, short splits): one wait, one
   // barrier, then each slice reduces its own stages.  Otherwise a pipeline of
-  // kLdsStages - 1 stages in flight, slice ks reducing stages ks, ks + KS, ...
+  // kLdsAhead stages in flight, slice ks reducing stages ks, ks + KS, ...
   const bool at_once = KS > 1 && nst <= kLdsStages;
   if (at_once) {
     for (int s = 0; s < nst; ++s) issue(s);
     wait_vmem_barrier<0>();
   } else {
-    for (int s = 0; s < kLdsStages - 1 && s < nst; ++s) issue(s);
+    for (int s = 0; s < kLdsAhead && s < nst; ++s) issue(s);
   }
   for (int s = at_once ? ks : 0; s < nst; s += at_once ? KS : 1) {
     if (!at_once) {
-      const int after = min(kLdsStages - 2, nst - 1 - s);
+      const int after = min(kLdsAhead - 1, nst - 1 - s);
       wait_stage_barrier<IPW>(after);
-      if (s + kLdsStages - 1 < nst) issue(s + kLdsStages - 1);
+      if (s + kLdsAhead < nst) issue(s + kLdsAhead);
       if (s % KS != ks) continue;
     }
     compute(s);

@@ -32,6 +32,11 @@
 namespace mtpv {
 
 constexpr int kNestRingStages = 5;
+// Code stages in flight ahead of the one being transcoded (as in the bf16
+// kernels, short memory queues pay: ragged batch KV8 955 -> 922 us with 2
+// instead of 4, llama3_8b_tree 23.5 -> 23.2 us; 3 changed nothing).
+constexpr int kNestAhead = 2;
+static_assert(kNestAhead >= 1 && kNestAhead <= kNestRingStages - 1, "ring slots refilled after their last read");
 constexpr int kNestCodeBytes = 8 * 1024 + 256;  // 8 code images + scales
 constexpr int kNestImgBytes = 16 * 1024;        // bf16 operand images of one stage
 
@@ -316,11 +321,13 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
     for (int t = 0; t < NT; ++t) st.acc[k][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // The ring keeps kNestRingStages - 1 stages ahead: the slot of stage s - 1
-  // (codes transcoded in iteration s - 2, scales read in iteration s - 1) is
-  // refilled in iteration s, after the barrier that ends those reads.
+  // The ring keeps kNestAhead <= kNestRingStages - 1 stages ahead: the slot
+  // refilled in iteration s (stage s + kNestAhead) last held stage
+  // s + kNestAhead - kNestRingStages <= s - 1 (codes transcoded in iteration
+  // s - 2, scales read in iteration s - 1), whose reads the barrier of
+  // iteration s has ended.
   if (ncs > 0) {
-    constexpr int kAhead = kNestRingStages - 1;
+    constexpr int kAhead = kNestAhead;
     for (int s = 0; s < kAhead && s < ncs; ++s) issue(s);
     // stage 0 landed (every later issued stage may still be in flight)
     wait_code_stage_barrier<PER>(min(kAhead, ncs) - 1);

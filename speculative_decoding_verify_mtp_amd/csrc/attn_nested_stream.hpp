@@ -38,7 +38,7 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
   constexpr int PER = CPW + 1;  // loads per wave per stage (codes + scales)
   constexpr int IPW = 16 / NR;  // operand images transcoded per wave
   constexpr int SL = kWave / NR;
-  constexpr int kAhead = kNestRingStages - 1;
+  constexpr int kAhead = kNestAhead;
   __shared__ __attribute__((aligned(16))) char ring[kNestRingStages * kNestCodeBytes];
   __shared__ __attribute__((aligned(16))) char img[2 * kNestImgBytes];
   __shared__ int s_pref[kStreamMaxB + 1];
