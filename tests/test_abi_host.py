@@ -161,6 +161,19 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
             want = -(-(-(-max_ctx // 32)) // 32) * 32
             S = max(S, min(cap, want))
     ns = -(-max_ctx // S) if max_ctx > 0 else 1
+    lds = dtype == lib.MTP_BF16 and R >= 16 and D == 128 and not stream
+    ks2 = lds and rb == 1 and nr <= 2 and S <= 32 * (5 - (W + 31) // 32)
+    if split == 0 and B == 1 and lds and not ks2:
+        # one sequence over two workgroups per CU (row blocks of one tile per
+        # wave): the first round's n1 splits hold S + d tokens, the rest
+        # S - d, d = 32 * round(S / 288)
+        nrb1 = -(-tiles // nr)
+        items = ns * Hkv * nrb1
+        n1 = 256 // (Hkv * nrb1)
+        d = 32 * int(S / 288 + 0.5)
+        if 256 < items <= 512 and n1 >= 1 and d > 0 and S + d <= 2048:
+            head = n1 * (S + d)
+            ns = -(-max_ctx // (S + d)) if max_ctx <= head else n1 + -(-(max_ctx - head) // (S - d))
     rows = B * ns * Hkv * R
     seg = 0
     if dtype == lib.MTP_BF16 and R >= 16 and D == 128 and 8 <= B <= 1024:
@@ -183,6 +196,8 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
 @pytest.mark.parametrize("kw", [
     dict(B=1, W=8, Hq=20, Hkv=5, D=128, dtype=1, max_ctx=4096),
     dict(B=1, W=32, Hq=32, Hkv=8, D=128, dtype=1, max_ctx=8192),
+    dict(B=1, W=32, Hq=32, Hkv=8, D=128, dtype=1, max_ctx=5000),
+    dict(B=1, W=16, Hq=32, Hkv=8, D=128, dtype=1, max_ctx=20000),
     dict(B=4, W=16, Hq=16, Hkv=16, D=64, dtype=1, max_ctx=16384),
     dict(B=64, W=16, Hq=32, Hkv=8, D=128, dtype=1, max_ctx=32768),
     dict(B=1, W=4, Hq=4, Hkv=4, D=64, dtype=0, max_ctx=256),
