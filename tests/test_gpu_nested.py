@@ -253,3 +253,72 @@ def test_nested_commit_bit_exact(skip_root):
     assert_planes_equal(kv.planes("k"), kp2, where, "K")
     assert_planes_equal(kv.planes("v"), vp2, where, "V")
     assert lib.device_status(clear=True) == 0
+
+
+# ----------------------------------------------------------------------------
+# data errors of the nested kernels: poisoned rows and the sticky status word
+# ----------------------------------------------------------------------------
+
+def nested_attn(inp, kv, recent=-1, max_ctx_len=None):
+    out, lse = lib.verify_attn_nested(inp["q"], kv, inp["block_table"], inp["ctx_lens"],
+                                      inp["k_new"], inp["v_new"], inp["mask_kind"],
+                                      inp["mask_ids"], kv8_recent=recent,
+                                      max_ctx_len=max_ctx_len, scale=inp["scale"])
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def assert_rest_close(inp, kp, vp, out, lse, rest, recent=-1):
+    ref_out, ref_lse = oracle_nested(inp, kp, vp, recent)
+    keep = torch.tensor(rest, device=out.device)
+    assert_attn_close(out[keep], lse[keep], ref_out[rest], ref_lse[rest], ATOL, RTOL, "rest")
+
+
+@pytest.mark.parametrize("B", [3, 9], ids=["split", "stream"])
+def test_nested_malformed_mask_poisons_only_that_sequence(B):
+    wl = W_("n_bad_mask", B=B, Hq=8, Hkv=2, W=8, ctx_lo=30, ctx_hi=300, masks="tree")
+    inp = gpu_inputs(wl, 21)
+    kv = quantized(inp)
+    kp, vp = oracle_planes(inp)
+    lib.device_status(clear=True)
+    ids = inp["mask_ids"].clone()
+    ids[1, 5] = 6  # a parent after its child
+    inp["mask_ids"] = ids
+    out, lse = nested_attn(inp, kv)
+    assert torch.isnan(out[1]).all() and torch.isnan(lse[1]).all()
+    assert_rest_close(inp, kp, vp, out, lse, [b for b in range(B) if b != 1])
+    assert lib.device_status(clear=True) & lib.DEV_BAD_MASK
+
+
+@pytest.mark.parametrize("B", [3, 9], ids=["split", "stream"])
+def test_nested_unmapped_committed_page_poisons_that_sequence(B):
+    wl = W_("n_bad_page", B=B, Hq=8, Hkv=2, W=8, ctx_lo=100, ctx_hi=400, masks="mixed")
+    inp = gpu_inputs(wl, 22)
+    kv = quantized(inp)
+    kp, vp = oracle_planes(inp)
+    lib.device_status(clear=True)
+    good = dict(inp)  # the oracle reads the unchanged table (sequence 0 is not compared)
+    bt = inp["block_table"].clone()
+    bt[0, 2] = kv.num_pages + 5
+    inp["block_table"] = bt
+    out, lse = nested_attn(inp, kv)
+    assert torch.isnan(out[0]).all()
+    assert_rest_close(good, kp, vp, out, lse, list(range(1, B)))
+    assert lib.device_status(clear=True) & lib.DEV_BAD_PAGE
+
+
+def test_nested_stream_context_above_bound_poisons_only_that_sequence():
+    wl = W_("n_bad_ctx", B=9, Hq=8, Hkv=2, W=8, ctx_lo=20, ctx_hi=300, masks="mixed")
+    inp = gpu_inputs(wl, 23)
+    kv = quantized(inp)
+    kp, vp = oracle_planes(inp)
+    ctx = [int(x) for x in inp["host"]["ctx_lens"]]
+    bound = max(ctx) - 1
+    lib.device_status(clear=True)
+    out, lse = nested_attn(inp, kv, recent=0, max_ctx_len=bound)
+    bad = [b for b in range(wl.B) if ctx[b] > bound]
+    rest = [b for b in range(wl.B) if ctx[b] <= bound]
+    assert bad and rest
+    assert torch.isnan(out[bad]).all() and torch.isnan(lse[bad]).all()
+    assert_rest_close(inp, kp, vp, out, lse, rest, recent=0)
+    assert lib.device_status(clear=True) & lib.DEV_BAD_CTX
