@@ -59,6 +59,7 @@ struct StreamParams {
   int rows_block;  // rows of a row block (NR * RB * 16)
   int h1 = 0;     // ranges per head in the first dispatch round (0: all ranges equal)
   int w_num = 1, w_den = 1;  // a first-round range is w_num / w_den times as long as the others
+  int piece_rows = 0;  // combine: one row per wave (segments of many pieces)
 };
 
 // Stage ranges of one head's list: ranges r < h1 hold t1 stages, the others

@@ -280,10 +280,104 @@ __device__ __forceinline__ void combine_rows_grouped(const AttnParams& p, const 
   }
 }
 
+// Stream layout with many pieces per segment (a few long sequences spread
+// over the whole grid: a segment then has one piece per range it crosses,
+// up to tens): one row per wave as in combine_rows, so that the row's pieces
+// are loaded in parallel rather than folded four at a time.  Pass 1 takes
+// the piece states over the lanes; pass 2 gives group q pieces q, q + 4, ...,
+// eight of them in flight at a time.  Waves loop over rows.
+template <int D>
+__device__ __forceinline__ void combine_stream_rows(const AttnParams& p, const StreamParams& sp,
+                                                    unsigned block, unsigned nblocks, int waves) {
+  constexpr int VPL = D / 16;  // columns per lane
+  constexpr int kBatch = 8;    // pieces per 16-lane group in flight
+  const int lane = threadIdx.x & 63;
+  const int gq = lane >> 4, gl = lane & 15;
+  const int wv = threadIdx.x >> 6;
+  if (wv >= waves) return;  // uniform over the wave
+  const size_t nrows = (size_t)p.B * p.W * p.Hq;
+  for (size_t row = (size_t)block * waves + wv; row < nrows; row += (size_t)nblocks * waves) {
+    const int h = (int)(row % p.Hq);
+    const size_t bw = row / p.Hq;
+    const int w = (int)(bw % p.W);
+    const int b = (int)(bw / p.W);
+    const int kvh = h / p.g;
+    const int rho = w * p.g + (h - kvh * p.g);
+    const int rb = rho / sp.rows_block;
+    const int sigma = b * sp.nseg + kvh * p.nRB + rb;
+    const int ns = sp.seg_info[2 * sigma + 1];
+    const size_t base = (size_t)sp.seg_info[2 * sigma] * sp.rows_block + (rho - rb * sp.rows_block);
+    const size_t stride = (size_t)sp.rows_block;
+    const int L = p.ctx_lens[b];
+    bool ok;
+    node_visibility(p.mask_kind[b], lane_mask_id(p, b, lane), p.W, p.lookback, lane, ok);
+    const bool ctx_ok = L >= 0 && L <= p.max_ctx;
+    float* o = p.out + row * D;
+    if (!ok || !ctx_ok) {
+      if (lane == 0 && w == 0 && h == 0)
+        raise_status((ok ? 0u : MTP_DEV_BAD_MASK) | (ctx_ok ? 0u : MTP_DEV_BAD_CTX));
+      for (int i = lane; i < D; i += kWave) o[i] = qnan();
+      if (p.lse != nullptr && lane == 0) p.lse[row] = qnan();
+      continue;
+    }
+    float M = neg_inf();
+    for (int s = lane; s < ns; s += kWave) M = fmaxf(M, p.part_ml[2 * (base + s * stride)]);
+    M = wave_max(M);
+    float wl = 0.f;
+    for (int s = lane; s < ns; s += kWave) {
+      const size_t i = base + s * stride;
+      wl += fast_exp2(p.part_ml[2 * i] - M) * p.part_ml[2 * i + 1];
+    }
+    const float den = wave_sum(wl);
+    float a[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) a[j] = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 4 * kBatch) {
+      float wt[kBatch];
+      float4 v[kBatch][VPL / 4];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int s = s0 + 4 * u + gq;
+        const int sl = s < ns ? s : 0;  // in range; dropped by its zero weight below
+        const size_t i = base + sl * stride;
+        wt[u] = p.part_ml[2 * i];
+        const float4* src = reinterpret_cast<const float4*>(p.part_acc + i * D + gl * VPL);
+#pragma unroll
+        for (int j = 0; j < VPL / 4; ++j) v[u][j] = src[j];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float wu = s0 + 4 * u + gq < ns ? fast_exp2(wt[u] - M) : 0.f;
+#pragma unroll
+        for (int j = 0; j < VPL / 4; ++j) {
+          a[4 * j] = fmaf(wu, v[u][j].x, a[4 * j]);
+          a[4 * j + 1] = fmaf(wu, v[u][j].y, a[4 * j + 1]);
+          a[4 * j + 2] = fmaf(wu, v[u][j].z, a[4 * j + 2]);
+          a[4 * j + 3] = fmaf(wu, v[u][j].w, a[4 * j + 3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) a[j] = rows4_sum(a[j]);
+    const float inv = 1.f / den;
+    if (gq == 0) {
+      f32x4* dst = reinterpret_cast<f32x4*>(o + gl * VPL);
+#pragma unroll
+      for (int j = 0; j < VPL / 4; ++j)
+        __builtin_nontemporal_store(f32x4{a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv,
+                                          a[4 * j + 3] * inv},
+                                    dst + j);
+    }
+    if (p.lse != nullptr && lane == 0) p.lse[row] = (M + log2f(den)) * kLn2;
+  }
+}
+
 template <int D, bool kStream>
 __global__ __launch_bounds__(256) void attn_combine(AttnParams p, StreamParams sp) {
-  if constexpr (kStream)
-    combine_rows_grouped<D, true>(p, sp, blockIdx.x, gridDim.x, blockDim.x >> 6);
+  if constexpr (kStream) {
+    if (sp.piece_rows) combine_stream_rows<D>(p, sp, blockIdx.x, gridDim.x, blockDim.x >> 6);
+    else combine_rows_grouped<D, true>(p, sp, blockIdx.x, gridDim.x, blockDim.x >> 6);
+  }
   else if (grouped_split_combine(p.max_splits, (long)p.B * p.W * p.Hq))
     combine_rows_grouped<D, false>(p, sp, blockIdx.x, gridDim.x, blockDim.x >> 6);
   else
@@ -306,8 +400,12 @@ __global__ __launch_bounds__(kAcceptThreads) void finish_kernel(AttnParams p, St
   __shared__ int sm[kAcceptScratchInts];
   if ((int)blockIdx.x < p.B)
     accept_commit_seq(ap, cp, (int)blockIdx.x, sm);
-  else if constexpr (kStream)
-    combine_rows_grouped<D, true>(p, sp, blockIdx.x - p.B, gridDim.x - p.B, combine_rows_per_block);
+  else if constexpr (kStream) {
+    if (sp.piece_rows)
+      combine_stream_rows<D>(p, sp, blockIdx.x - p.B, gridDim.x - p.B, combine_rows_per_block);
+    else
+      combine_rows_grouped<D, true>(p, sp, blockIdx.x - p.B, gridDim.x - p.B, combine_rows_per_block);
+  }
   else
     combine_rows<D>(p, blockIdx.x - p.B, combine_rows_per_block);
 }

@@ -137,6 +137,7 @@ mtp_status build_attn(const mtp_shape* shape, const void* q, const void* k_cache
   a.sp.h1 = pl.h1;
   a.sp.w_num = kFirstRoundNum;
   a.sp.w_den = kFirstRoundDen;
+  a.sp.piece_rows = pl.piece_rows ? 1 : 0;
   return MTP_OK;
 }
 
@@ -197,11 +198,12 @@ void launch_partial(const Attn& a, int D, int dtype, int B, hipStream_t strm,
 }
 
 // Output rows one combine wave takes: four (one per 16-lane group) for the
-// stream layout and for split layouts with few splits, one otherwise.
-// `finish`: the step's finish launch (grouped for the stream layout only).
+// stream layout with few pieces per segment and for split layouts with few
+// splits, one otherwise.  `finish`: the step's finish launch (grouped for
+// the stream layout only).
 bool grouped_combine(const AttnParams& p, const Plan& pl, bool finish) {
-  return stream_layout(pl.kernel) ||
-         (!finish && grouped_split_combine(pl.max_splits, (long)p.B * p.W * p.Hq));
+  if (stream_layout(pl.kernel)) return !pl.piece_rows;
+  return !finish && grouped_split_combine(pl.max_splits, (long)p.B * p.W * p.Hq);
 }
 int combine_rows_per_wave(const AttnParams& p, const Plan& pl, bool finish) {
   return grouped_combine(p, pl, finish) ? 4 : 1;

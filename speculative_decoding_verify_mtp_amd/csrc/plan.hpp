@@ -46,8 +46,14 @@ constexpr long kMinStreamStages = 2;
 // workgroups per CU; ragged batch: equal ranges 900 us, first-round share of
 // the list 0.53 / 0.55 / 0.57 / 0.59: 882 / 872 / 878 / 908 us).
 constexpr int kFirstRoundNum = 5, kFirstRoundDen = 4;
-// A handful of sequences is balanced by the split plan already, and the
-// stream kernel's per-workgroup set-up would dominate their short ranges.
+// Fewer than kStreamMinB sequences take the stream kernel when its ranges
+// would hold at least this many stages.
+constexpr long kMinRangeStages = 4;
+// Stream-layout combine: segments of at most this many pieces (estimated)
+// are folded four rows per wave, longer ones one row per wave.
+constexpr long kGroupedMaxPieces = 12;
+// Batches of at least this many sequences take the stream kernel; fewer
+// do when its ranges are long enough (kMinRangeStages).
 constexpr int kStreamMinB = 8;
 
 struct Plan {
@@ -63,6 +69,7 @@ struct Plan {
   int max_splits;  // splits of the longest context
   int G;           // stream kernel: workgroups
   int h1;          // stream kernel: ranges per head in the first dispatch round (0: equal ranges)
+  bool piece_rows; // stream layout with many pieces per segment: the combine takes a row per wave
   int nts, nseg, rows_block;
   size_t acc_bytes, ml_offset, ml_bytes, seg_offset, seg_bytes;
 };
@@ -140,8 +147,20 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
     pl.S = S < kMinSplit ? kMinSplit : (S > kMaxSplit ? kMaxSplit : S);
   }
   pl.nts = (s.W + 31) / 32;
-  const bool stream_shape = (pl.kernel == kMfmaLds || pl.kernel == kMfmaNested) && s.B >= kStreamMinB &&
-                            s.B <= kStreamMaxB;
+  bool stream_shape = (pl.kernel == kMfmaLds || pl.kernel == kMfmaNested) && s.B >= kStreamMinB &&
+                      s.B <= kStreamMaxB;
+  // Fewer sequences with one row tile per wave: the stream schedule still
+  // pays once each of its ranges holds a few stages (whole steps: one
+  // sequence of 32000 tokens 52.0 -> 42.9 us, two of 8000 33.9 -> 29.0 us,
+  // four of 16000 77.1 -> 74.2 us; one of 4096 with 32 rows per head, about
+  // two stages per range, 14.4 -> 18.6 us, so it stays per split).
+  if (pl.kernel == kMfmaLds && s.B >= 1 && s.B < kStreamMinB && pl.RB == 1 && s.split_tokens == 0) {
+    const long seg_stages = (long)(s.max_ctx_len + 31) / 32 + pl.nts;
+    const long upper_h = (long)s.B * pl.nRB * seg_stages;
+    const long slots_h = std::max(1L, (long)kCUs * kStreamWgsPerCU / s.Hkv);
+    const long Gh = std::max(1L, std::min((upper_h + kMinStreamStages - 1) / kMinStreamStages, slots_h));
+    stream_shape = upper_h >= kMinRangeStages * Gh;
+  }
   // Per-split LDS kernel with one or two row tiles per workgroup: two key
   // slices (each wave reduces half of the stages) when every stage of a split
   // fits the ring.  The automatic split then also grows, within the ring, until
@@ -160,6 +179,7 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
   pl.max_splits = num_splits(s.max_ctx_len, pl.S, 0, pl.S);
   pl.G = 0;
   pl.h1 = 0;
+  pl.piece_rows = false;
   pl.nseg = s.Hkv * pl.nRB;
   pl.rows_block = 16 * pl.NR * pl.RB;
   size_t rows = (size_t)s.B * pl.max_splits * s.Hkv * pl.R;
@@ -196,6 +216,9 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
       // Two workgroups per CU: the G - 256 workgroups past the first round
       // share CUs with first-round ones, whose ranges are made longer.
       if (s.split_tokens == 0 && pl.RB == 1 && pl.G > kCUs) pl.h1 = kCUs / s.Hkv;
+      // pieces per segment: about one per range the segment crosses
+      const long per_seg = (pl.G / s.Hkv + (long)s.B * pl.nRB - 1) / ((long)s.B * pl.nRB) + 1;
+      pl.piece_rows = per_seg > kGroupedMaxPieces;
       rows = ((size_t)pl.G + (size_t)s.B * pl.nseg) * pl.rows_block;
     }
   }

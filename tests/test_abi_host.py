@@ -153,6 +153,11 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
     else:
         S = split
     stream = dtype == lib.MTP_BF16 and R >= 16 and D == 128 and 8 <= B <= 1024
+    if dtype == lib.MTP_BF16 and R >= 16 and D == 128 and 1 <= B < 8 and rb == 1 and not split:
+        # fewer sequences: the stream kernel when its ranges hold >= 4 stages
+        upper_h = B * nrb * (-(-max_ctx // 32) + -(-W // 32))
+        gh = max(1, min(-(-upper_h // 2), max(1, 512 // Hkv)))
+        stream = upper_h >= 4 * gh
     if dtype == lib.MTP_BF16 and R >= 16 and D == 128 and not stream and rb == 1 and nr <= 2:
         # key slices: a split whose stages all fit the 5-stage ring; the
         # automatic split grows (within it) to at most 32 splits per row
@@ -176,7 +181,7 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
             ns = -(-max_ctx // (S + d)) if max_ctx <= head else n1 + -(-(max_ctx - head) // (S - d))
     rows = B * ns * Hkv * R
     seg = 0
-    if dtype == lib.MTP_BF16 and R >= 16 and D == 128 and 8 <= B <= 1024:
+    if stream:
         # stream kernel: G = Hkv * Gh persistent workgroups (Gh ranges per KV
         # head), pieces <= G + segments
         nseg = Hkv * nrb

@@ -143,6 +143,39 @@ STREAM_WEIGHTED = [
 ]
 
 
+# Few sequences over the whole grid: 256 ranges per KV head cross each
+# segment, and the combine takes one row per wave.
+STREAM_MANY_PIECES = [
+    W_("stream_pieces_hkv2", B=8, Hq=32, Hkv=2, W=4, ctx_lo=2000, ctx_hi=4000, masks="mixed"),
+    W_("stream_pieces_w16", B=9, Hq=16, Hkv=1, W=4, ctx_lo=100, ctx_hi=3000, masks="tree"),
+]
+
+
+@pytest.mark.parametrize("wl", STREAM_MANY_PIECES, ids=[w.name for w in STREAM_MANY_PIECES])
+def test_stream_many_pieces_per_segment(wl):
+    inp = gpu_inputs(wl, 29)
+    out, lse = run_attn(inp)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
+
+
+# Fewer than eight sequences, one row tile per wave, ranges of at least four
+# stages: the stream kernel (and its row-per-wave combine).
+SMALL_BATCH_STREAM = [
+    W_("stream_b1", B=1, Hq=32, Hkv=8, W=16, ctx_lo=9000, ctx_hi=9000, masks="chain"),
+    W_("stream_b2_hkv5", B=2, Hq=20, Hkv=5, W=8, ctx_lo=8000, ctx_hi=8000, masks="tree"),
+    W_("stream_b3_mixed", B=3, Hq=32, Hkv=8, W=16, ctx_lo=3000, ctx_hi=6000, masks="mixed"),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL_BATCH_STREAM, ids=[w.name for w in SMALL_BATCH_STREAM])
+def test_small_batch_stream(wl):
+    inp = gpu_inputs(wl, 31)
+    out, lse = run_attn(inp)
+    ref_out, ref_lse = oracle_attn(inp)
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
+
+
 @pytest.mark.parametrize("wl", STREAM_WEIGHTED, ids=[w.name for w in STREAM_WEIGHTED])
 def test_stream_weighted_ranges(wl):
     inp = gpu_inputs(wl, 19)
@@ -599,6 +632,11 @@ def test_empty_batch_is_a_no_op():
 STEP = [
     W_("step_mixed_b9", B=9, Hq=32, Hkv=8, W=16, ctx_lo=0, ctx_hi=700, masks="mixed"),
     W_("step_stream_straddle", B=9, Hq=3, Hkv=1, W=11, ctx_lo=10, ctx_hi=400, masks="mixed"),
+    # 256 ranges per KV head over 8 sequences: the finish launch's combine
+    # takes one row per wave
+    W_("step_stream_pieces", B=8, Hq=32, Hkv=2, W=4, ctx_lo=1500, ctx_hi=3000, masks="mixed"),
+    # one long sequence on the stream kernel
+    W_("step_stream_b1", B=1, Hq=32, Hkv=8, W=16, ctx_lo=9000, ctx_hi=9000, masks="tree"),
     W_("step_grouped_b4", B=4, Hq=64, Hkv=8, W=16, ctx_lo=50, ctx_hi=600, masks="mixed"),
     W_("step_chain_b1", B=1, Hq=20, Hkv=5, W=8, ctx_lo=600, ctx_hi=600),
     W_("step_segment_d64", B=3, Hq=16, Hkv=16, D=64, W=16, ctx_lo=30, ctx_hi=300,
