@@ -153,8 +153,10 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
   // pays once each of its ranges holds a few stages (whole steps: one
   // sequence of 32000 tokens 52.0 -> 42.9 us, two of 8000 33.9 -> 29.0 us,
   // four of 16000 77.1 -> 74.2 us; one of 4096 with 32 rows per head, about
-  // two stages per range, 14.4 -> 18.6 us, so it stays per split).
-  if (pl.kernel == kMfmaLds && s.B >= 1 && s.B < kStreamMinB && pl.RB == 1 && s.split_tokens == 0) {
+  // two stages per range, 14.4 -> 18.6 us, so it stays per split).  The
+  // nested kernels alike (attention: 49.1 -> 41.3 us, 32.9 -> 29.2 us).
+  if ((pl.kernel == kMfmaLds || pl.kernel == kMfmaNested) && s.B >= 1 && s.B < kStreamMinB &&
+      pl.RB == 1 && s.split_tokens == 0) {
     const long seg_stages = (long)(s.max_ctx_len + 31) / 32 + pl.nts;
     const long upper_h = (long)s.B * pl.nRB * seg_stages;
     const long slots_h = std::max(1L, (long)kCUs * kStreamWgsPerCU / s.Hkv);

@@ -143,6 +143,9 @@ NESTED_STREAM = [
     W_("ns_r16", B=10, Hq=8, Hkv=4, W=8, ctx_lo=15, ctx_hi=300, masks="mixed"),
     # 33 rows per sequence and head (a padded tile), segments with lookback 1
     W_("ns_r33", B=8, Hq=3, Hkv=1, W=11, ctx_lo=0, ctx_hi=500, masks="segment", seg_lookback=1),
+    # fewer sequences whose ranges hold four or more stages
+    W_("ns_b1", B=1, Hq=32, Hkv=8, W=16, ctx_lo=9000, ctx_hi=9000, masks="chain"),
+    W_("ns_b2", B=2, Hq=32, Hkv=8, W=16, ctx_lo=5000, ctx_hi=8000, masks="mixed"),
 ]
 
 
