@@ -701,7 +701,7 @@ def main() -> int:
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": warm_steps,
+        "warmup": R + wreps * NG,
         "warmup_requested": args.warmup,
         "ms_per_step": round(sec_per_step * 1e3, 5),
         "higher_is_better": True,
@@ -717,7 +717,8 @@ def main() -> int:
         "ms_per_step_gpu_events": round(step_ms_events, 5),
         "ms_per_step_spread": spread,
         "timing": f"{args.steps} steps: {reps} HIP graph replays of {NG} steps (step j reads KV "
-                  f"replica j % {R}) + a graph of {tail}, after {wreps * NG} untimed steps; "
+                  f"replica j % {R}) + a graph of {tail}, after {R} eager and {wreps * NG} graph-replayed "
+                  f"untimed steps; "
                   f"wall clock around the timed replays; partial kernel from events around "
                   f"{preps} replays of a graph of {NG} partial launches",
         "kv_bytes_per_step": nbytes["kv"],

@@ -6,9 +6,21 @@
 // partial piece per (range, segment); the workgroup holding a segment's first
 // stage records its pieces for the combine), with the stage work of
 // attn_partial_nested_lds: committed stages stream through the code ring and
-// are transcoded once per workgroup into double-buffered bf16 operand images;
-// the accumulators hold sum_t p_t s_t u_t (u = c8 + 136) beside
-// lp = sum_t p_t s_t until the offset is removed.  That correction is linear
+// are transcoded once per workgroup into double-buffered operand images.  The
+// byte u = c8 + 136 of an element goes into the MFMA as the bf16 bit pattern
+// 0x00uu, which is u * 2^-133 exactly for every u in [0, 255] (below 128 a
+// subnormal, from 128 the first normal binade, whose spacing is the same), so
+// a code becomes an operand by a byte permute, with no conversion:
+//   K images: four v_perm per 8 elements;
+//   V images: the bytes themselves (8 per lane), spread into bf16 pairs by the
+//   same permutes that pair the keys of the PV operand.
+// Q enters the committed stages scaled by 2^e (a power of two per row, so that
+// |Q 2^e| lies in [2^120, 2^121): the products with u * 2^-133 stay in the
+// normal fp32 range), the factor 2^(133 - e) moving into the row's softmax
+// scale; P enters scaled by 2^60 (an offset in the exp), for the same reason
+// on the PV side.  The accumulators hold 2^-73 sum_t p_t s_t u_t beside
+// lp = 2^60 sum_t p_t s_t and a row sum scaled by 2^60 until the offset is
+// removed.  That correction is linear
 // in the state and commutes with later rescales, so it is applied once per
 // segment part, when the part's committed stages are followed by in-block
 // stages or when the piece is written.  A segment's in-block stages (bf16
@@ -27,6 +39,110 @@
 
 namespace mtpv {
 
+// One stage's operand images: 8 K images of 1 KB (bf16 bit patterns 0x00uu),
+// then 8 V byte images of 512 bytes.
+constexpr int kNestImgBytesU = 8 * 1024 + 8 * 512;
+constexpr float kNestPBias = 60.f;  // log2 of the scale of P in the committed stages
+
+// K operand image dword k (elements 2k, 2k + 1) from the bytes u of the even
+// (ev) and odd (od) elements: bf16 bit patterns 0x00uu.
+__device__ __forceinline__ uint4 nest_k_operand(unsigned ev, unsigned od) {
+  return make_uint4(__builtin_amdgcn_perm(od, ev, 0x0c040c00u), __builtin_amdgcn_perm(od, ev, 0x0c050c01u),
+                    __builtin_amdgcn_perm(od, ev, 0x0c060c02u), __builtin_amdgcn_perm(od, ev, 0x0c070c03u));
+}
+
+// Scores and softmax of one committed stage with the byte operands: as
+// nest_scores, with the row's own scale sl2r (the 2^(133 - e) of its Q
+// scaling folded in) and P scaled by 2^kNestPBias.
+template <int RB>
+__device__ __forceinline__ void nest_scores_u(const bf16x8 (&qs)[RB][4], const bf16x8 (&kf)[2][4],
+                                              const float (&skv)[8], float (&svv)[8],
+                                              const float (&nqs)[RB], const float (&sl2r)[RB], int nk,
+                                              MfmaState<128, RB>& st, float (&lp)[RB],
+                                              bf16x8 (&pf)[RB], bf16x8 (&pl)[RB]) {
+  const int qd = (threadIdx.x & 63) >> 4;
+  float x[RB][8];
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][m], qs[k][m], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][m], qs[k][m], s1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[k][e] = skv[e] * (s0[e] + nqs[k]);
+      x[k][4 + e] = skv[4 + e] * (s1[e] + nqs[k]);
+    }
+  }
+  if (nk < 32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (pv_key(qd, e) >= nk) {
+        svv[e] = 0.f;
+#pragma unroll
+        for (int k = 0; k < RB; ++k) x[k][e] = neg_inf();
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < RB; ++k) {
+    float mx = max8(x[k]);
+    mx = rows4_max(mx);
+    mx *= sl2r[k];
+    const float mold = st.m[k];
+    const float mref = mx > mold + kRescaleSlack ? mx : mold;
+    const float muse = mref == neg_inf() ? 0.f : mref;
+    const float bias = kNestPBias - muse;
+    float pe[8], pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = fast_exp2(fmaf(x[k][e], sl2r[k], bias));
+      pv[e] = pe[e] * svv[e];
+    }
+    const float sum = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+    const float sump = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    if (__ballot(mref != mold) != 0ull) {
+      const float alpha = fast_exp2(mold - muse);
+      st.l[k] *= alpha;
+      lp[k] *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) st.acc[k][t] *= alpha;
+    }
+    st.l[k] += sum;
+    lp[k] += sump;
+    st.m[k] = mref;
+    split_bf16_hi_lo(pv, pf[k], pl[k]);
+  }
+}
+
+// PV accumulate of one committed stage from the V byte vectors (vb[e]: bytes
+// u of d = 8c + 0, 2, 4, 6 in .x and 8c + 1, 3, 5, 7 in .y, key pv_key(q, e)):
+// operand t pairs element t of keys 2j and 2j + 1 as bf16 bit patterns 0x00uu.
+template <int RB>
+__device__ __forceinline__ void tile_pv_u(const bf16x8 (&pf)[RB], const bf16x8 (&pl)[RB],
+                                          const uint2 (&vb)[8], MfmaState<128, RB>& st) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const unsigned sel = 0x0c040c00u + (unsigned)(t >> 1) * 0x00010001u;
+    unsigned w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned x = (t & 1) ? vb[2 * j].y : vb[2 * j].x;
+      const unsigned y = (t & 1) ? vb[2 * j + 1].y : vb[2 * j + 1].x;
+      w[j] = __builtin_amdgcn_perm(y, x, sel);
+    }
+    bf16x8 a;
+    __builtin_memcpy(&a, w, sizeof(a));
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      st.acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[k], st.acc[k][t], 0, 0, 0);
+      st.acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[k], st.acc[k][t], 0, 0, 0);
+    }
+  }
+}
+
 template <int NR, bool KV4>
 __global__ __launch_bounds__(64 * NR) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
@@ -40,7 +156,7 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
   constexpr int SL = kWave / NR;
   constexpr int kAhead = kNestAhead;
   __shared__ __attribute__((aligned(16))) char ring[kNestRingStages * kNestCodeBytes];
-  __shared__ __attribute__((aligned(16))) char img[2 * kNestImgBytes];
+  __shared__ __attribute__((aligned(16))) char img[2 * kNestImgBytesU];
   __shared__ int s_pref[kStreamMaxB + 1];
 
   const int wg = (int)blockIdx.x;
@@ -64,7 +180,7 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
   const int Hkv = p.Hkv;
   const uint32_t ring_base = lds_offset(ring);
   const size_t slot_stride = (size_t)Hkv * D;
-  const float sl2 = p.scale_log2 * 0.0625f;  // the key scales enter as s, not s / 16
+  const float sl2 = p.scale_log2 * 0.0625f;  // the key scales enter as s, not s / 16 (before the Q scaling)
   // code image lane l <- key (l % 16) ^ (l / 16), part l / 16
   const int dkey = c ^ qd;
   const uint32_t doff = 64u * dkey + 16u * qd;
@@ -78,22 +194,26 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
   MfmaState<D, RB> st;
   float lp[RB];
   bool coded = false;  // acc and lp in code units (offset not yet removed)
-  bf16x8 qf[RB][NC];
-  float nqs[RB];
+  bf16x8 qf[RB][NC];  // Q operands (in-block stages)
+  bf16x8 qs[RB][NC];  // Q 2^e (committed stages)
+  float nqs[RB];      // -136 sum_d q_d, times 2^(e - 133)
+  float sl2r[RB];     // sl2 2^(133 - e)
   uint64_t vrow[RB];
   int cur_sigma = -1;
   bool bad = false;
 
-  // acc <- (acc - 136 lp) / 16: the committed keys' values in real units
+  // acc <- (2^73 acc - 136 2^-60 lp) / 16 and the row sum <- 2^-60 l: the
+  // committed keys' values and weights in real units
   auto settle = [&]() {
     if (!coded) return;
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
-      const float off = -kNestByteOffset * 0.0625f * rows4_sum(lp[k]);
+      const float off = -kNestByteOffset * 0.0625f * 0x1p-60f * rows4_sum(lp[k]);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.acc[k][t][e] = fmaf(st.acc[k][t][e], 0.0625f, off);
+        for (int e = 0; e < 4; ++e) st.acc[k][t][e] = fmaf(st.acc[k][t][e], 0x1p69f, off);
+      st.l[k] *= 0x1p-60f;
       lp[k] = 0.f;
     }
     coded = false;
@@ -148,7 +268,20 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
 #pragma unroll
           for (int m = 0; m < NC; ++m) qf[k][m] = bf16x8{};
         }
-        nqs[k] = -kNestByteOffset * rows4_sum(part);
+        // the power of two 2^e that puts the row's largest |q| in [2^120, 2^121)
+        float amax = 0.f;
+#pragma unroll
+        for (int m = 0; m < NC; ++m)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qf[k][m][e]));
+        amax = rows4_max(amax);
+        const int ex = amax > 0.f ? 121 - __builtin_amdgcn_frexp_expf(amax) : 120;
+#pragma unroll
+        for (int m = 0; m < NC; ++m)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qs[k][m][e] = (__bf16)ldexpf((float)qf[k][m][e], ex);
+        nqs[k] = ldexpf(-kNestByteOffset * rows4_sum(part), ex - 133);
+        sl2r[k] = ldexpf(sl2, 133 - ex);
         vrow[k] = 0;
       }
       if (i0 == 0 && threadIdx.x == 0) {
@@ -239,7 +372,7 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
     };
     auto transcode = [&](int s) __attribute__((always_inline)) {
       const char* code = ring + (s % kNestRingStages) * kNestCodeBytes;
-      char* out = img + (s & 1) * kNestImgBytes + 16 * lane;
+      char* out = img + (s & 1) * kNestImgBytesU;
       const int t0 = 32 * (i0 + s);
 #pragma unroll
       for (int k = 0; k < IPW; ++k) {
@@ -268,9 +401,10 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
         }
         unsigned ev, od;
         nest_bytes(bw, rw, ev, od);
-        *reinterpret_cast<uint4*>(out + im * 1024) =
-            make_uint4(pack_bf16_exact(ubyte<0>(ev), ubyte<0>(od)), pack_bf16_exact(ubyte<1>(ev), ubyte<1>(od)),
-                       pack_bf16_exact(ubyte<2>(ev), ubyte<2>(od)), pack_bf16_exact(ubyte<3>(ev), ubyte<3>(od)));
+        if (im < 8)
+          *reinterpret_cast<uint4*>(out + im * 1024 + 16 * lane) = nest_k_operand(ev, od);
+        else
+          *reinterpret_cast<uint2*>(out + 8192 + (im - 8) * 512 + 8 * lane) = make_uint2(ev, od);
       }
     };
     if (ncr > 0) {
@@ -285,7 +419,8 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
         if (s + kAhead < ncr) issue(s + kAhead);
         if (s + 1 < ncr) transcode(s + 1);
 
-        const char* buf = img + (s & 1) * kNestImgBytes + lane * 16;
+        const char* buf = img + (s & 1) * kNestImgBytesU + lane * 16;
+        const char* vbuf = img + (s & 1) * kNestImgBytesU + 8192 + lane * 8;
         const char* code = ring + (s % kNestRingStages) * kNestCodeBytes;
         bf16x8 kf[2][NC];
 #pragma unroll
@@ -293,9 +428,9 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
 #pragma unroll
           for (int m = 0; m < NC; ++m)
             kf[kt][m] = *reinterpret_cast<const bf16x8*>(buf + (kt * 4 + m) * 1024);
-        VRow<D> vv[8];
+        uint2 vb[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vv[e].v = *reinterpret_cast<const uint4*>(buf + (8 + e) * 1024);
+        for (int e = 0; e < 8; ++e) vb[e] = *reinterpret_cast<const uint2*>(vbuf + e * 512);
         const float4 sk0 = *reinterpret_cast<const float4*>(code + 8192 + 16 * qd);
         const float4 sk1 = *reinterpret_cast<const float4*>(code + 8192 + 64 + 16 * qd);
         const float4 sv0 = *reinterpret_cast<const float4*>(code + 8192 + 128 + 16 * qd);
@@ -304,8 +439,8 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
         float svv[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
         const int nk = L - 32 * (i0 + s);
         bf16x8 pf[RB], pl[RB];
-        nest_scores<RB>(qf, kf, skv, svv, nqs, sl2, nk, st, lp, pf, pl);
-        tile_pv<D, RB>(pf, pl, vv, st);
+        nest_scores_u<RB>(qs, kf, skv, svv, nqs, sl2r, nk, st, lp, pf, pl);
+        tile_pv_u<RB>(pf, pl, vb, st);
       }
       // every wave is done with the ring and the images before they are reused
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
