@@ -100,6 +100,26 @@ struct MfmaState {
 // relative to the reference stay below 2^8, far from fp32 overflow.
 constexpr float kRescaleSlack = 8.f;
 
+// Log2-domain weights pe[e] = 2^(x[e] s - m + bias) of eight scores against
+// the reference m (the rounded product mx s of the largest raw score mx, or
+// an earlier one).  While |m| < 2^20 one fma per weight: its exact product
+// differs from the rounded one by less than 2^-3.  Beyond, the product is
+// rounded first, so that the argument of the largest score is exactly its
+// distance to the reference: with an fma, half an ulp of a product above
+// 2^31 would overflow the exponential (NaN rows for very large scores).
+// The choice is wave-uniform.
+__device__ __forceinline__ void log2_weights(const float (&x)[8], float s, float m, float bias,
+                                             float (&pe)[8]) {
+  if (__ballot(fabsf(m) > 0x1p20f) == 0ull) {
+    const float c = bias - m;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(fmaf(x[e], s, c));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = fast_exp2((mul_rn(x[e], s) - m) + bias);
+  }
+}
+
 // Largest of eight scores.  IEEE maximum (NaN-propagating) maps to gfx950's
 // three-input v_maximum3_f32 and, unlike fmaxf, needs no quieting of the
 // MFMA results first; the masked scores are -inf, never NaN.  (Used by the
@@ -177,16 +197,17 @@ __device__ __forceinline__ void tile_softmax(float (&x)[RB][8], float scale_log2
       if (!vis(k, e)) x[k][e] = neg_inf();
     float mx = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
                      fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
-    mx = rows4_max(mx);
-    mx *= scale_log2;
+    mx = mul_rn(rows4_max(mx), scale_log2);
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
     const float muse = mref == neg_inf() ? 0.f : mref;
     float sum = 0.f;
     __bf16 ph[8], plo[8];
+    float pw[8];
+    log2_weights(x[k], scale_log2, muse, 0.f, pw);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(fmaf(x[k][e], scale_log2, -muse));
+      const float pe = pw[e];
       sum += pe;
       ph[e] = (__bf16)pe;
       plo[e] = (__bf16)(pe - (float)ph[e]);

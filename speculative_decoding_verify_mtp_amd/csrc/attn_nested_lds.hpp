@@ -116,18 +116,14 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
   }
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
-    float mx = max8(x[k]);
-    mx = rows4_max(mx);
-    mx *= sl2;
+    const float mx = mul_rn(rows4_max(max8(x[k])), sl2);
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
     const float muse = mref == neg_inf() ? 0.f : mref;
     float pe[8], pv[8];
+    log2_weights(x[k], sl2, muse, 0.f, pe);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pe[e] = fast_exp2(fmaf(x[k][e], sl2, -muse));
-      pv[e] = pe[e] * svv[e];
-    }
+    for (int e = 0; e < 8; ++e) pv[e] = pe[e] * svv[e];
     const float sum = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
     const float sump = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     if (__ballot(mref != mold) != 0ull) {

@@ -18,9 +18,10 @@
 // |Q 2^e| lies in [2^120, 2^121): the products with u * 2^-133 stay in the
 // normal fp32 range), the factor 2^(133 - e) moving into the row's softmax
 // scale; P enters scaled by 2^60 (an offset in the exp), for the same reason
-// on the PV side.  The accumulators hold 2^-73 sum_t p_t s_t u_t beside
-// lp = 2^60 sum_t p_t s_t and a row sum scaled by 2^60 until the offset is
-// removed.  That correction is linear
+// on the PV side: products of V scales down to about 2^-50 (|v| ~ 1e-14)
+// stay normal, and P 2^60 s stays below the bf16 limit for s < 2^60.  The
+// accumulators hold 2^-73 sum_t p_t s_t u_t and the row sum 2^60 sum_t p_t
+// until the offset is removed; lp = sum_t p_t s_t is kept in real units.  That correction is linear
 // in the state and commutes with later rescales, so it is applied once per
 // segment part, when the part's committed stages are followed by in-block
 // stages or when the piece is written.  A segment's in-block stages (bf16
@@ -88,19 +89,14 @@ __device__ __forceinline__ void nest_scores_u(const bf16x8 (&qs)[RB][4], const b
   }
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
-    float mx = max8(x[k]);
-    mx = rows4_max(mx);
-    mx *= sl2r[k];
+    const float mx = mul_rn(rows4_max(max8(x[k])), sl2r[k]);
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
     const float muse = mref == neg_inf() ? 0.f : mref;
-    const float bias = kNestPBias - muse;
     float pe[8], pv[8];
+    log2_weights(x[k], sl2r[k], muse, kNestPBias, pe);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pe[e] = fast_exp2(fmaf(x[k][e], sl2r[k], bias));
-      pv[e] = pe[e] * svv[e];
-    }
+    for (int e = 0; e < 8; ++e) pv[e] = pe[e] * svv[e];
     const float sum = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
     const float sump = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     if (__ballot(mref != mold) != 0ull) {
@@ -111,7 +107,7 @@ __device__ __forceinline__ void nest_scores_u(const bf16x8 (&qs)[RB][4], const b
       for (int t = 0; t < 8; ++t) st.acc[k][t] *= alpha;
     }
     st.l[k] += sum;
-    lp[k] += sump;
+    lp[k] = fmaf(sump, 0x1p-60f, lp[k]);  // in real units: lp stays far from overflow
     st.m[k] = mref;
     split_bf16_hi_lo(pv, pf[k], pl[k]);
   }
@@ -202,13 +198,13 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
   int cur_sigma = -1;
   bool bad = false;
 
-  // acc <- (2^73 acc - 136 2^-60 lp) / 16 and the row sum <- 2^-60 l: the
+  // acc <- (2^73 acc - 136 lp) / 16 and the row sum <- 2^-60 l: the
   // committed keys' values and weights in real units
   auto settle = [&]() {
     if (!coded) return;
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
-      const float off = -kNestByteOffset * 0.0625f * 0x1p-60f * rows4_sum(lp[k]);
+      const float off = -kNestByteOffset * 0.0625f * rows4_sum(lp[k]);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll

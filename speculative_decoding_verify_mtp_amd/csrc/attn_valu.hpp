@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams p) {
       for (int i = 0; i < 16; ++i) s = fmaf(qv[r][i], kf[i], s);
 #pragma unroll
       for (int o = 1; o < LPK; o <<= 1) s += __shfl_xor(s, o);
-      s *= p.scale_log2;
+      s = mul_rn(s, p.scale_log2);  // the max and the exponent see the same rounded score
       const bool vis = valid && (jb < 0 || ((vrow[r] >> jb) & 1ull) != 0ull);
       if (vis) {
         const float mn = fmaxf(m[r], s);

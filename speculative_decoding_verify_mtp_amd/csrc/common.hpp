@@ -44,6 +44,15 @@ __device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
 // 2^x on the transcendental unit; exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x * y rounded to fp32 and kept out of fp contraction: where one product is
+// both compared (a running maximum) and subtracted from it inside an
+// exponential, an fma would subtract from the exact product, leaving up to
+// half an ulp of it (above 2^31 enough to overflow the exponential).
+__device__ __forceinline__ float mul_rn(float x, float y) {
+#pragma clang fp contract(off)
+  return x * y;
+}
+
 __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
   const unsigned lo = __shfl((unsigned)v, src);
   const unsigned hi = __shfl((unsigned)(v >> 32), src);

@@ -166,6 +166,40 @@ def test_nested_stream_attention_matches_oracle(wl, recent):
     assert lib.device_status(clear=True) == 0
 
 
+# Magnitudes far from N(0, 1): the stream kernel scales Q by a power of two
+# per row and P by 2^60 so that its products with the code bytes (operand bit
+# patterns 0x00uu = u 2^-133) stay in the normal fp32 range.  Attention is
+# linear in V and the softmax sees only q.k, so each case compares out / v
+# scale with the standard tolerance.  Two workloads: the stream kernel (nine
+# sequences) and the per-split kernel (two).
+EXTREME = [(1e-30, 1.0, 1.0), (1e30, 1.0, 1.0), (1.0, 1e-20, 1.0), (1.0, 1e12, 1.0),
+           (1.0, 1.0, 1e-12), (1.0, 1.0, 1e16)]
+
+
+@pytest.mark.parametrize("qs,ks,vs", EXTREME, ids=[f"q{a:g}_k{b:g}_v{c:g}" for a, b, c in EXTREME])
+@pytest.mark.parametrize("B", [9, 2])
+def test_nested_extreme_magnitudes(B, qs, ks, vs):
+    wl = W_("n_extreme", B=B, Hq=16, Hkv=4, W=8, ctx_lo=20, ctx_hi=900, masks="mixed")
+    inp = gpu_inputs(wl, 31)
+    inp["q"].mul_(qs)
+    for key, f in (("k_cache", ks), ("k_new", ks), ("v_cache", vs), ("v_new", vs)):
+        inp[key].mul_(f)
+    kv = quantized(inp)
+    kp, vp = oracle_planes(inp)
+    for recent in (-1, 0):
+        out, lse = lib.verify_attn_nested(inp["q"], kv, inp["block_table"], inp["ctx_lens"],
+                                          inp["k_new"], inp["v_new"], inp["mask_kind"],
+                                          inp["mask_ids"], kv8_recent=recent,
+                                          max_ctx_len=int(inp["host"]["ctx_lens"].max()),
+                                          scale=inp["scale"], seg_lookback=inp["seg_lookback"])
+        torch.cuda.synchronize()
+        assert lib.device_status(clear=True) == 0
+        ref_out, ref_lse = oracle_nested(inp, kp, vp, recent)
+        assert np.isfinite(out.cpu().numpy()).all(), f"B={B} q{qs} k{ks} v{vs}: non-finite output"
+        assert_attn_close(out / vs, lse, ref_out / vs, ref_lse, ATOL, RTOL,
+                          f"B={B} q{qs} k{ks} v{vs} recent={recent}")
+
+
 @pytest.mark.parametrize("split", [32, 96, 1024])
 def test_nested_stream_work_split_does_not_change_the_result(split):
     """Workgroups of 1, 3 or 32 stages: ranges start and end inside

@@ -69,6 +69,40 @@ def test_attention_matches_oracle_small(wl):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=wl.name)
 
 
+# Magnitudes far from N(0, 1).  Very large scores used to overflow the
+# exponential (an fma's exact product against the rounded reference max left
+# a residual of half an ulp, above 2^31 more than the exponent range) and gave
+# NaN rows; tiny ones must not vanish.  Attention is linear in V and the
+# softmax sees only q.k, so each case compares out / (V scale).  One
+# workload per kernel family: the stream kernel (nine sequences), the
+# per-split LDS kernel (two), the D = 64 direct-load kernel and the fp32 VALU
+# kernel.
+EXTREME = [(1e-30, 1.0, 1.0), (1e30, 1.0, 1.0), (1.0, 1e-20, 1.0), (1.0, 1e12, 1.0),
+           (1.0, 1.0, 1e-20), (1.0, 1.0, 1e20)]
+EXTREME_WL = [
+    W_("x_stream", B=9, Hq=16, Hkv=4, W=8, ctx_lo=20, ctx_hi=900, masks="mixed"),
+    W_("x_lds", B=2, Hq=16, Hkv=4, W=8, ctx_lo=20, ctx_hi=900, masks="mixed"),
+    W_("x_d64", B=2, Hq=16, Hkv=16, D=64, W=16, ctx_lo=20, ctx_hi=600, masks="segment",
+       seg_lookback=1),
+    W_("x_fp32", B=2, Hq=4, Hkv=4, D=64, W=4, dtype="f32", ctx_lo=20, ctx_hi=300),
+]
+
+
+@pytest.mark.parametrize("qs,ks,vs", EXTREME, ids=[f"q{a:g}_k{b:g}_v{c:g}" for a, b, c in EXTREME])
+@pytest.mark.parametrize("wl", EXTREME_WL, ids=[w.name for w in EXTREME_WL])
+def test_extreme_magnitudes(wl, qs, ks, vs):
+    inp = gpu_inputs(wl, 33)
+    inp["q"].mul_(qs)
+    for key, f in (("k_cache", ks), ("k_new", ks), ("v_cache", vs), ("v_new", vs)):
+        inp[key].mul_(f)
+    out, lse = run_attn(inp)
+    assert lib.device_status(clear=True) == 0
+    ref_out, ref_lse = oracle_attn(inp)
+    assert np.isfinite(out.cpu().numpy()).all(), f"{wl.name} q{qs} k{ks} v{vs}: non-finite output"
+    assert_attn_close(out / vs, lse, ref_out / vs, ref_lse, *tol_for(wl),
+                      what=f"{wl.name} q{qs} k{ks} v{vs}")
+
+
 @pytest.mark.parametrize("split", [32, 64, 96, 128, 2048])
 def test_split_size_does_not_change_the_result(split):
     wl = W_("splits", B=3, Hq=16, Hkv=4, W=8, ctx_lo=1, ctx_hi=700, masks="mixed")
