@@ -8,11 +8,18 @@
 //   (l % 16) ^ (l / 16), part l / 16 (bytes [16 part, +16) of its 64-byte row):
 //   the XOR spreads the reads of the transcode over the LDS banks.
 //   1 scale image of 256 bytes: K scales of the 32 keys, then V scales.
-// Every stage is transcoded once per workgroup into the sixteen bf16 operand
-// images of the bf16 LDS kernel (images 0-7: K operands, 8-15: V vectors),
-// holding u = c8 + 136 exactly (see nested.hpp); the waves then run the same
-// MFMA step with the per-key scales applied to the scores and to P, and the
-// offset removed at the end.  Operand images are double buffered: at
+// Every stage is transcoded once per workgroup into operand images: the
+// byte u = c8 + 136 of an element (nested.hpp) taken as the bf16 bit pattern
+// 0x00uu, which is u 2^-133 exactly for every u in [0, 255] (below 128 a
+// subnormal, from 128 the first normal binade, with the same spacing; gfx950's
+// bf16 MFMA takes both exactly).  K images (0-7, the operand layout of the bf16
+// LDS kernel) are four byte permutes per 8 elements; V images (8-15) keep the
+// bytes themselves, 8 per lane, and the PV step spreads them into bf16 pairs
+// with the permutes that pair its keys anyway.  The products stay in the
+// normal fp32 range because Q enters scaled by 2^e per row (nest_scale_q) and
+// P by 2^kNestPBias; the waves run the MFMA step of the bf16 kernel with the
+// per-key scales applied to the scores and to P, and the offset and both
+// powers of two removed at the end.  Operand images are double buffered: at
 // iteration s one barrier proves that stage s + 1's codes have landed, that
 // the operands of stage s are complete and that nobody reads the other
 // operand buffer any more; then stage s + 1 is transcoded while stage s is
@@ -38,7 +45,6 @@ constexpr int kNestRingStages = 5;
 constexpr int kNestAhead = 2;
 static_assert(kNestAhead >= 1 && kNestAhead <= kNestRingStages - 1, "ring slots refilled after their last read");
 constexpr int kNestCodeBytes = 8 * 1024 + 256;  // 8 code images + scales
-constexpr int kNestImgBytes = 16 * 1024;        // bf16 operand images of one stage
 
 // 4 bytes from global `g` into LDS at m0 + 4 * lane, m0 = lds (wave-uniform).
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
@@ -74,20 +80,34 @@ __device__ __forceinline__ void wait_code_stage_barrier(int n) {
     wait_vmem_lds_barrier<3 * PER>();
 }
 
+// One stage's operand images: 8 K images of 1 KB (bf16 bit patterns 0x00uu),
+// then 8 V byte images of 512 bytes.
+constexpr int kNestImgBytesU = 8 * 1024 + 8 * 512;
+constexpr float kNestPBias = 60.f;  // log2 of the scale of P in the committed stages
+
+// K operand image dword k (elements 2k, 2k + 1) from the bytes u of the even
+// (ev) and odd (od) elements: bf16 bit patterns 0x00uu.
+__device__ __forceinline__ uint4 nest_k_operand(unsigned ev, unsigned od) {
+  return make_uint4(__builtin_amdgcn_perm(od, ev, 0x0c040c00u), __builtin_amdgcn_perm(od, ev, 0x0c050c01u),
+                    __builtin_amdgcn_perm(od, ev, 0x0c060c02u), __builtin_amdgcn_perm(od, ev, 0x0c070c03u));
+}
+
 // Scores and softmax of one committed stage for the RB row tiles of a wave.
-// skv / svv: the raw scales of the lane's keys pv_key(q, 0..7); sl2 = the
-// softmax scale * log2(e) / 16 (so x * sl2 is the log2-domain score);
-// P' = p * s_v (sixteen times p * s_v / 16: the 1/16 is applied with the
-// offset at the end).  Keys past nk (the last stage of a split) are masked
-// by selection and their V scales zeroed (a slot never written holds
-// arbitrary scales; p = 0 must not meet a NaN).  One code path for full and partial stages: with a specialised
-// copy for each, the compiler copied every accumulator register per stage.
+// qs: the row tiles' scaled Q operands (nest_scale_q); kf: the K operand
+// images (bit patterns 0x00uu); skv / svv: the raw scales of the lane's keys
+// pv_key(q, 0..7); sl2r: the row's log2-domain scale (softmax scale * log2(e)
+// / 16, times the 2^(133 - e) of its Q scaling).  P' = 2^kNestPBias p s_v
+// goes to the PV product as bf16 hi + lo; the row sum carries the same
+// 2^kNestPBias, lp = sum_t p_t s_t is kept in real units.  Keys past nk (the
+// last stage of a split or range) are masked by selection and their V scales
+// zeroed (a slot never written holds arbitrary scales; p = 0 must not meet a
+// NaN).  One code path for full and partial stages.
 template <int RB>
-__device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf16x8 (&kf)[2][4],
-                                            const float (&skv)[8], float (&svv)[8],
-                                            const float (&nqs)[RB], float sl2, int nk,
-                                            MfmaState<128, RB>& st, float (&lp)[RB],
-                                            bf16x8 (&pf)[RB], bf16x8 (&pl)[RB]) {
+__device__ __forceinline__ void nest_scores_u(const bf16x8 (&qs)[RB][4], const bf16x8 (&kf)[2][4],
+                                              const float (&skv)[8], float (&svv)[8],
+                                              const float (&nqs)[RB], const float (&sl2r)[RB], int nk,
+                                              MfmaState<128, RB>& st, float (&lp)[RB],
+                                              bf16x8 (&pf)[RB], bf16x8 (&pl)[RB]) {
   const int qd = (threadIdx.x & 63) >> 4;
   float x[RB][8];
 #pragma unroll
@@ -95,8 +115,8 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][m], qf[k][m], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][m], qf[k][m], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][m], qs[k][m], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][m], qs[k][m], s1, 0, 0, 0);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -116,12 +136,12 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
   }
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
-    const float mx = mul_rn(rows4_max(max8(x[k])), sl2);
+    const float mx = mul_rn(rows4_max(max8(x[k])), sl2r[k]);
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
     const float muse = mref == neg_inf() ? 0.f : mref;
     float pe[8], pv[8];
-    log2_weights(x[k], sl2, muse, 0.f, pe);
+    log2_weights(x[k], sl2r[k], muse, kNestPBias, pe);
 #pragma unroll
     for (int e = 0; e < 8; ++e) pv[e] = pe[e] * svv[e];
     const float sum = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
@@ -134,10 +154,59 @@ __device__ __forceinline__ void nest_scores(const bf16x8 (&qf)[RB][4], const bf1
       for (int t = 0; t < 8; ++t) st.acc[k][t] *= alpha;
     }
     st.l[k] += sum;
-    lp[k] += sump;
+    lp[k] = fmaf(sump, 0x1p-60f, lp[k]);  // in real units: lp stays far from overflow
     st.m[k] = mref;
     split_bf16_hi_lo(pv, pf[k], pl[k]);
   }
+}
+
+// PV accumulate of one committed stage from the V byte vectors (vb[e]: bytes
+// u of d = 8c + 0, 2, 4, 6 in .x and 8c + 1, 3, 5, 7 in .y, key pv_key(q, e)):
+// operand t pairs element t of keys 2j and 2j + 1 as bf16 bit patterns 0x00uu.
+template <int RB>
+__device__ __forceinline__ void tile_pv_u(const bf16x8 (&pf)[RB], const bf16x8 (&pl)[RB],
+                                          const uint2 (&vb)[8], MfmaState<128, RB>& st) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const unsigned sel = 0x0c040c00u + (unsigned)(t >> 1) * 0x00010001u;
+    unsigned w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned x = (t & 1) ? vb[2 * j].y : vb[2 * j].x;
+      const unsigned y = (t & 1) ? vb[2 * j + 1].y : vb[2 * j + 1].x;
+      w[j] = __builtin_amdgcn_perm(y, x, sel);
+    }
+    bf16x8 a;
+    __builtin_memcpy(&a, w, sizeof(a));
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      st.acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[k], st.acc[k][t], 0, 0, 0);
+      st.acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[k], st.acc[k][t], 0, 0, 0);
+    }
+  }
+}
+
+// Committed-stage Q operands of one row tile: Q 2^e (exact), e putting the
+// row's largest |q| in [2^120, 2^121), so that the products with the operand
+// bit patterns 0x00uu = u 2^-133 stay in the normal fp32 range; the factor
+// 2^(133 - e) moves into the row's softmax scale (sl2r) and into the offset
+// term nqs = -136 sum_d q_d 2^(e - 133).  qsum: this lane's share of
+// sum_d q_d.
+__device__ __forceinline__ void nest_scale_q(const bf16x8 (&qf)[4], float qsum, float sl2,
+                                             bf16x8 (&qs)[4], float& nqs, float& sl2r) {
+  float amax = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qf[m][e]));
+  amax = rows4_max(amax);
+  const int ex = amax > 0.f ? 121 - __builtin_amdgcn_frexp_expf(amax) : 120;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qs[m][e] = (__bf16)ldexpf((float)qf[m][e], ex);
+  nqs = ldexpf(-kNestByteOffset * rows4_sum(qsum), ex - 133);
+  sl2r = ldexpf(sl2, 133 - ex);
 }
 
 template <int RB, int NR>
@@ -151,7 +220,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
   constexpr int IPW = 16 / NR;       // operand images transcoded per wave
   constexpr int SL = kWave / NR;     // scale lanes per wave
   __shared__ __attribute__((aligned(16))) char ring[kNestRingStages * kNestCodeBytes];
-  __shared__ __attribute__((aligned(16))) char img[2 * kNestImgBytes];
+  __shared__ __attribute__((aligned(16))) char img[2 * kNestImgBytesU];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -167,8 +236,11 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
   int pr0 = lane < pavail ? btrow[lane] : 0;
   int pr1 = lane + 64 < pavail ? btrow[lane + 64] : 0;
   const int row_tile0 = (it.rb * NR + wv) * RB;
-  bf16x8 qf[RB][NC];
-  float nqs[RB];  // -136 * sum_d q_d of this lane's row
+  bf16x8 qf[RB][NC];  // Q operands (in-block keys)
+  bf16x8 qs[RB][NC];  // Q 2^e (committed keys)
+  float nqs[RB];      // -136 sum_d q_d of this lane's row, times 2^(e - 133)
+  float sl2r[RB];     // the row's log2-domain scale for the committed keys
+  const float sl2 = p.scale_log2 * 0.0625f;  // the key scales enter as s, not s / 16
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
     const int rho = (row_tile0 + k) * 16 + c;
@@ -188,8 +260,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
 #pragma unroll
       for (int m = 0; m < NC; ++m) qf[k][m] = bf16x8{};
     }
-    part = rows4_sum(part);
-    nqs[k] = -kNestByteOffset * part;
+    nest_scale_q(qf[k], part, sl2, qs[k], nqs[k], sl2r[k]);
   }
 
   // the mask description goes out with the set-up loads: the last split
@@ -211,7 +282,6 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
   if ((unsigned)pr1 >= (unsigned)p.num_pages) pr1 = 0;
   const int kv8_from = na.kv8_recent < 0 ? 0 : max(0, L - na.kv8_recent);
   const int ncs = (end - start + 31) / 32;
-  const float sl2 = p.scale_log2 * 0.0625f;  // the key scales enter as s, not s / 16
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- code stage issue: this wave's code images and its share of the scales
@@ -266,12 +336,11 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
   // ---- transcode stage s: this wave's operand images into buffer s % 2
   auto transcode = [&](int s) __attribute__((always_inline)) {
     const char* code = ring + (s % kNestRingStages) * kNestCodeBytes;
-    char* out = img + (s & 1) * kNestImgBytes + 16 * lane;
+    char* out = img + (s & 1) * kNestImgBytesU;
     const int t0 = start + 32 * s;
 #pragma unroll
     for (int k = 0; k < IPW; ++k) {
       const int im = wv + NR * k;
-      unsigned w[4];
       if (im < 8) {
         // K operand (kt, m): key 16 kt + c, elements [32 m + 8 qd, +8) = part m, dword qd
         const int kt = im >> 2, m = im & 3;
@@ -281,10 +350,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
         if (t0 + 16 * kt + c < kv8_from) rw = kNestZeroRef;
         unsigned ev, od;
         nest_bytes(bw, rw, ev, od);
-        w[0] = pack_bf16_exact(ubyte<0>(ev), ubyte<0>(od));
-        w[1] = pack_bf16_exact(ubyte<1>(ev), ubyte<1>(od));
-        w[2] = pack_bf16_exact(ubyte<2>(ev), ubyte<2>(od));
-        w[3] = pack_bf16_exact(ubyte<3>(ev), ubyte<3>(od));
+        *reinterpret_cast<uint4*>(out + im * 1024 + 16 * lane) = nest_k_operand(ev, od);
       } else {
         // V vector e: key pv_key(qd, e), elements [8 c, +8) = part c / 4, dword c % 4
         const int e = im - 8;
@@ -297,12 +363,8 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
         if (t0 + 16 * half + k16 < kv8_from) rw = kNestZeroRef;
         unsigned ev, od;
         nest_bytes(bw, rw, ev, od);
-        w[0] = pack_bf16_exact(ubyte<0>(ev), ubyte<0>(od));
-        w[1] = pack_bf16_exact(ubyte<1>(ev), ubyte<1>(od));
-        w[2] = pack_bf16_exact(ubyte<2>(ev), ubyte<2>(od));
-        w[3] = pack_bf16_exact(ubyte<3>(ev), ubyte<3>(od));
+        *reinterpret_cast<uint2*>(out + 8192 + (im - 8) * 512 + 8 * lane) = make_uint2(ev, od);
       }
-      *reinterpret_cast<uint4*>(out + im * 1024) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
 
@@ -335,7 +397,8 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
       if (s + kAhead < ncs) issue(s + kAhead);
       if (s + 1 < ncs) transcode(s + 1);
 
-      const char* buf = img + (s & 1) * kNestImgBytes + lane * 16;
+      const char* buf = img + (s & 1) * kNestImgBytesU + lane * 16;
+      const char* vbuf = img + (s & 1) * kNestImgBytesU + 8192 + lane * 8;
       const char* code = ring + (s % kNestRingStages) * kNestCodeBytes;
       bf16x8 kf[2][NC];
 #pragma unroll
@@ -343,9 +406,9 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
 #pragma unroll
         for (int m = 0; m < NC; ++m)
           kf[kt][m] = *reinterpret_cast<const bf16x8*>(buf + (kt * 4 + m) * 1024);
-      uint4 vraw[8];
+      uint2 vb[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vraw[e] = *reinterpret_cast<const uint4*>(buf + (8 + e) * 1024);
+      for (int e = 0; e < 8; ++e) vb[e] = *reinterpret_cast<const uint2*>(vbuf + e * 512);
       // scales / 16 of the lane's keys pv_key(qd, 0..7)
       const float4 sk0 = *reinterpret_cast<const float4*>(code + 8192 + 16 * qd);
       const float4 sk1 = *reinterpret_cast<const float4*>(code + 8192 + 64 + 16 * qd);
@@ -355,25 +418,21 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
       float svv[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
       const int nk = end - (start + 32 * s);
       bf16x8 pf[RB], pl[RB];
-      nest_scores<RB>(qf, kf, skv, svv, nqs, sl2, nk, st, lp, pf, pl);
-      VRow<D> vv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vv[e].v = vraw[e];
-      tile_pv<D, RB>(pf, pl, vv, st);
+      nest_scores_u<RB>(qs, kf, skv, svv, nqs, sl2r, nk, st, lp, pf, pl);
+      tile_pv_u<RB>(pf, pl, vb, st);
     }
   }
 
-  // acc holds sum_t p_t s_t u_t: the committed part of the output row is
-  // (acc - 136 sum_t p_t s_t) / 16
+  // acc holds 2^-73 sum_t p_t s_t u_t and the row sum 2^60 sum_t p_t: the
+  // committed part of the output row is (2^73 acc - 136 sum_t p_t s_t) / 16
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
-    float lrow = lp[k];
-    lrow = rows4_sum(lrow);
-    const float off = -kNestByteOffset * 0.0625f * lrow;
+    const float off = -kNestByteOffset * 0.0625f * rows4_sum(lp[k]);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st.acc[k][t][e] = fmaf(st.acc[k][t][e], 0.0625f, off);
+      for (int e = 0; e < 4; ++e) st.acc[k][t][e] = fmaf(st.acc[k][t][e], 0x1p69f, off);
+    st.l[k] *= 0x1p-60f;
   }
 
   // in-block keys (bf16), masked per row, in the last split: direct loads

@@ -40,105 +40,6 @@
 
 namespace mtpv {
 
-// One stage's operand images: 8 K images of 1 KB (bf16 bit patterns 0x00uu),
-// then 8 V byte images of 512 bytes.
-constexpr int kNestImgBytesU = 8 * 1024 + 8 * 512;
-constexpr float kNestPBias = 60.f;  // log2 of the scale of P in the committed stages
-
-// K operand image dword k (elements 2k, 2k + 1) from the bytes u of the even
-// (ev) and odd (od) elements: bf16 bit patterns 0x00uu.
-__device__ __forceinline__ uint4 nest_k_operand(unsigned ev, unsigned od) {
-  return make_uint4(__builtin_amdgcn_perm(od, ev, 0x0c040c00u), __builtin_amdgcn_perm(od, ev, 0x0c050c01u),
-                    __builtin_amdgcn_perm(od, ev, 0x0c060c02u), __builtin_amdgcn_perm(od, ev, 0x0c070c03u));
-}
-
-// Scores and softmax of one committed stage with the byte operands: as
-// nest_scores, with the row's own scale sl2r (the 2^(133 - e) of its Q
-// scaling folded in) and P scaled by 2^kNestPBias.
-template <int RB>
-__device__ __forceinline__ void nest_scores_u(const bf16x8 (&qs)[RB][4], const bf16x8 (&kf)[2][4],
-                                              const float (&skv)[8], float (&svv)[8],
-                                              const float (&nqs)[RB], const float (&sl2r)[RB], int nk,
-                                              MfmaState<128, RB>& st, float (&lp)[RB],
-                                              bf16x8 (&pf)[RB], bf16x8 (&pl)[RB]) {
-  const int qd = (threadIdx.x & 63) >> 4;
-  float x[RB][8];
-#pragma unroll
-  for (int k = 0; k < RB; ++k) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][m], qs[k][m], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][m], qs[k][m], s1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[k][e] = skv[e] * (s0[e] + nqs[k]);
-      x[k][4 + e] = skv[4 + e] * (s1[e] + nqs[k]);
-    }
-  }
-  if (nk < 32) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (pv_key(qd, e) >= nk) {
-        svv[e] = 0.f;
-#pragma unroll
-        for (int k = 0; k < RB; ++k) x[k][e] = neg_inf();
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < RB; ++k) {
-    const float mx = mul_rn(rows4_max(max8(x[k])), sl2r[k]);
-    const float mold = st.m[k];
-    const float mref = mx > mold + kRescaleSlack ? mx : mold;
-    const float muse = mref == neg_inf() ? 0.f : mref;
-    float pe[8], pv[8];
-    log2_weights(x[k], sl2r[k], muse, kNestPBias, pe);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = pe[e] * svv[e];
-    const float sum = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-    const float sump = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-    if (__ballot(mref != mold) != 0ull) {
-      const float alpha = fast_exp2(mold - muse);
-      st.l[k] *= alpha;
-      lp[k] *= alpha;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) st.acc[k][t] *= alpha;
-    }
-    st.l[k] += sum;
-    lp[k] = fmaf(sump, 0x1p-60f, lp[k]);  // in real units: lp stays far from overflow
-    st.m[k] = mref;
-    split_bf16_hi_lo(pv, pf[k], pl[k]);
-  }
-}
-
-// PV accumulate of one committed stage from the V byte vectors (vb[e]: bytes
-// u of d = 8c + 0, 2, 4, 6 in .x and 8c + 1, 3, 5, 7 in .y, key pv_key(q, e)):
-// operand t pairs element t of keys 2j and 2j + 1 as bf16 bit patterns 0x00uu.
-template <int RB>
-__device__ __forceinline__ void tile_pv_u(const bf16x8 (&pf)[RB], const bf16x8 (&pl)[RB],
-                                          const uint2 (&vb)[8], MfmaState<128, RB>& st) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const unsigned sel = 0x0c040c00u + (unsigned)(t >> 1) * 0x00010001u;
-    unsigned w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned x = (t & 1) ? vb[2 * j].y : vb[2 * j].x;
-      const unsigned y = (t & 1) ? vb[2 * j + 1].y : vb[2 * j + 1].x;
-      w[j] = __builtin_amdgcn_perm(y, x, sel);
-    }
-    bf16x8 a;
-    __builtin_memcpy(&a, w, sizeof(a));
-#pragma unroll
-    for (int k = 0; k < RB; ++k) {
-      st.acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[k], st.acc[k][t], 0, 0, 0);
-      st.acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[k], st.acc[k][t], 0, 0, 0);
-    }
-  }
-}
-
 template <int NR, bool KV4>
 __global__ __launch_bounds__(64 * NR) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
@@ -264,20 +165,7 @@ void attn_partial_nested_stream(AttnParams p, StreamParams sp, NestedAttn na) {
 #pragma unroll
           for (int m = 0; m < NC; ++m) qf[k][m] = bf16x8{};
         }
-        // the power of two 2^e that puts the row's largest |q| in [2^120, 2^121)
-        float amax = 0.f;
-#pragma unroll
-        for (int m = 0; m < NC; ++m)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qf[k][m][e]));
-        amax = rows4_max(amax);
-        const int ex = amax > 0.f ? 121 - __builtin_amdgcn_frexp_expf(amax) : 120;
-#pragma unroll
-        for (int m = 0; m < NC; ++m)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qs[k][m][e] = (__bf16)ldexpf((float)qf[k][m][e], ex);
-        nqs[k] = ldexpf(-kNestByteOffset * rows4_sum(part), ex - 133);
-        sl2r[k] = ldexpf(sl2, 133 - ex);
+        nest_scale_q(qf[k], part, sl2, qs[k], nqs[k], sl2r[k]);
         vrow[k] = 0;
       }
       if (i0 == 0 && threadIdx.x == 0) {

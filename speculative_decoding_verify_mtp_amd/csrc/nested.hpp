@@ -9,12 +9,11 @@
 //   Codes are stored + 8 as nibbles, two per byte, even element low:
 //   base / ref planes [pages, Hkv, 16, D/2] bytes, scales [pages, Hkv, 16] fp32.
 //
-// Dequantization for the MFMA operands: with both nibbles of an element, the
-// byte 16 (q4 + 8) + (qr + 8) = c8 + 136, c8 = 16 q4 + qr, is built for four
-// elements at a time with two masks and a shift, converted exactly to float
-// (v_cvt_f32_ubyte) and packed to bf16 (exact: at most 8 significant bits).
-// The MFMA products therefore see u = c8 + 136 instead of c8; the offset is
-// removed in fp32:
+// Codes as MFMA operands: with both nibbles of an element, the byte
+// u = 16 (q4 + 8) + (qr + 8) = c8 + 136, c8 = 16 q4 + qr, is built for four
+// elements at a time with two masks and a shift, and enters the bf16 MFMA as
+// the bit pattern 0x00uu, which is exactly u 2^-133 (attn_nested_lds.hpp).
+// The products therefore see u instead of c8; the offset is removed in fp32:
 //   scores: q.k = (s_k / 16) (sum_d q_d u_d - 136 sum_d q_d) per key,
 //   values: sum_t p_t v_t = (sum_t p_t s_t u_t - 136 sum_t p_t s_t) / 16,
 // with sum_d q_d computed once per row and sum_t p_t s_t kept beside the row
@@ -146,16 +145,6 @@ __global__ __launch_bounds__(256) void commit_nested_kernel(NestedCommitParams p
 __device__ __forceinline__ void nest_bytes(unsigned b, unsigned r, unsigned& ev, unsigned& od) {
   ev = ((b & 0x0F0F0F0Fu) << 4) | (r & 0x0F0F0F0Fu);
   od = (b & 0xF0F0F0F0u) | ((r >> 4) & 0x0F0F0F0Fu);
-}
-
-template <int K>
-__device__ __forceinline__ float ubyte(unsigned w) {
-  return (float)((w >> (8 * K)) & 0xFFu);  // v_cvt_f32_ubyte<K>
-}
-
-// bf16 pair (lo, hi) of two floats whose low 16 bits are zero.
-__device__ __forceinline__ unsigned pack_bf16_exact(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 struct NestedAttn {
