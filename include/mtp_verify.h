@@ -329,7 +329,9 @@ mtp_status mtp_verify_attn_nested_workspace_size(const mtp_shape* shape, size_t*
  * t >= L - kv8_recent ("Recent-N"), else in KV4; kv8_recent = 0 reads the
  * base plane only (drafting), and then k_ref / v_ref may be NULL.  The
  * block's own rows (k_new, v_new) are used unquantized.  Results match
- * attention over the dequantized cache within the bf16 tolerance. */
+ * attention over the dequantized cache within the bf16 tolerance for
+ * committed V scales s below 2^60 (max|v| below about 8e18; beyond, the
+ * scaled weights overflow and the row comes out non-finite). */
 mtp_status mtp_verify_attn_nested(const mtp_shape* shape, const void* q, const mtp_nested_kv* kv,
                                   const int32_t* block_table, const int32_t* ctx_lens,
                                   const void* k_new, const void* v_new, const uint8_t* mask_kind,
