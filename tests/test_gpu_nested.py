@@ -200,6 +200,26 @@ def test_nested_extreme_magnitudes(B, qs, ks, vs):
                           f"B={B} q{qs} k{ks} v{vs} recent={recent}")
 
 
+@pytest.mark.parametrize("B", [1024, 1100])
+def test_nested_batch_at_and_above_the_stream_table(B):
+    """1024 sequences fill the nested stream kernel's stage table exactly;
+    more run the per-split nested kernel."""
+    wl = W_(f"n_b{B}", B=B, Hq=4, Hkv=1, W=4, ctx_lo=0, ctx_hi=40, masks="mixed", spare_pages=8)
+    inp = gpu_inputs(wl, 16)
+    kv = quantized(inp)
+    kp, vp = oracle_planes(inp)
+    for recent in (-1, 0):
+        out, lse = lib.verify_attn_nested(inp["q"], kv, inp["block_table"], inp["ctx_lens"],
+                                          inp["k_new"], inp["v_new"], inp["mask_kind"],
+                                          inp["mask_ids"], kv8_recent=recent,
+                                          max_ctx_len=int(inp["host"]["ctx_lens"].max()),
+                                          scale=inp["scale"], seg_lookback=inp["seg_lookback"])
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle_nested(inp, kp, vp, recent)
+        assert_attn_close(out, lse, ref_out, ref_lse, ATOL, RTOL, f"B={B} recent={recent}")
+        assert lib.device_status(clear=True) == 0
+
+
 @pytest.mark.parametrize("split", [32, 96, 1024])
 def test_nested_stream_work_split_does_not_change_the_result(split):
     """Workgroups of 1, 3 or 32 stages: ranges start and end inside

@@ -125,14 +125,16 @@ def test_valu_long_splits_match_oracle(split, dtype):
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"valu split {split} {dtype}")
 
 
-def test_batch_above_the_stream_table_uses_per_split_items():
-    """More than 1024 sequences: the per-split LDS kernel instead of the
-    stream schedule (its stage table holds 1024 sequences)."""
-    wl = W_("b1100", B=1100, Hq=4, Hkv=1, W=4, ctx_lo=0, ctx_hi=40, masks="mixed", spare_pages=8)
+@pytest.mark.parametrize("B", [1024, 1100])
+def test_batch_at_and_above_the_stream_table(B):
+    """1024 sequences fill the stream schedule's stage table exactly; more
+    run the per-split LDS kernel instead."""
+    wl = W_(f"b{B}", B=B, Hq=4, Hkv=1, W=4, ctx_lo=0, ctx_hi=40, masks="mixed", spare_pages=8)
     inp = gpu_inputs(wl, 6)
     out, lse = run_attn(inp)
     ref_out, ref_lse = oracle_attn(inp)
-    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what="B=1100")
+    assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"B={B}")
+    assert lib.device_status(clear=True) == 0
 
 
 @pytest.mark.parametrize("split", [32, 256, 1024])
