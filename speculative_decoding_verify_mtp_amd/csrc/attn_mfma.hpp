@@ -123,9 +123,10 @@ __device__ __forceinline__ void log2_weights(const float (&x)[8], float s, float
 // Largest of eight scores.  IEEE maximum (NaN-propagating) maps to gfx950's
 // three-input v_maximum3_f32 and, unlike fmaxf, needs no quieting of the
 // MFMA results first; the masked scores are -inf, never NaN.  (Used by the
-// nested-cache kernel: 1110 -> 1089 us with this and split_bf16_hi_lo on the
-// ragged batch; the bf16 stream kernel measured 915 -> 928 us with them and
-// keeps fmaxf and per-value conversions.)
+// nested-cache kernels, 1110 -> 1089 us with this and split_bf16_hi_lo on the
+// ragged batch, and by the lean tile_softmax; the bf16 stream kernel measured
+// 915 -> 928 us and 879 -> 892 us with them and keeps fmaxf and per-value
+// conversions.)
 __device__ __forceinline__ float max8(const float (&x)[8]) {
   const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), x[2]);
   const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3], x[4]), x[5]);
@@ -181,7 +182,12 @@ __device__ __forceinline__ void tile_scores(const bf16x8 (&qf)[RB][D / 32],
 // reference max moves, and the tile's probabilities as the PV product's
 // operand (P^T, bf16 hi + lo parts).  vis(k, e) tells whether row tile k may
 // see key e of this lane's 8 keys.
-template <int D, int RB, typename VisFn>
+// kLean: the row max by three-input IEEE maxima and the hi + lo parts by
+// packed conversions (fewer instructions: per-split and direct kernels,
+// llama3_8b_tree 18.0 -> 17.6 us, bitnet2b_chain 9.23 -> 9.13 us,
+// lca_segments 54.2 -> 53.6 us); the stream kernel keeps the other form
+// (ragged batch 879 us against 892 us lean).
+template <int D, int RB, bool kLean = true, typename VisFn>
 __device__ __forceinline__ void tile_softmax(float (&x)[RB][8], float scale_log2,
                                              MfmaState<D, RB>& st, bf16x8 (&pf)[RB],
                                              bf16x8 (&pl)[RB], VisFn vis) {
@@ -195,22 +201,34 @@ __device__ __forceinline__ void tile_softmax(float (&x)[RB][8], float scale_log2
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (!vis(k, e)) x[k][e] = neg_inf();
-    float mx = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
-                     fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
-    mx = mul_rn(rows4_max(mx), scale_log2);
+    float mx;
+    if constexpr (kLean) {
+      mx = mul_rn(rows4_maximum(max8(x[k])), scale_log2);
+    } else {
+      mx = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
+                 fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
+      mx = mul_rn(rows4_max(mx), scale_log2);
+    }
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
     const float muse = mref == neg_inf() ? 0.f : mref;
-    float sum = 0.f;
-    __bf16 ph[8], plo[8];
     float pw[8];
     log2_weights(x[k], scale_log2, muse, 0.f, pw);
+    float sum = 0.f;
+    if constexpr (kLean) {
+      sum = ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+      split_bf16_hi_lo(pw, pf[k], pl[k]);
+    } else {
+      __bf16 ph[8], plo[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = pw[e];
-      sum += pe;
-      ph[e] = (__bf16)pe;
-      plo[e] = (__bf16)(pe - (float)ph[e]);
+      for (int e = 0; e < 8; ++e) {
+        const float pe = pw[e];
+        sum += pe;
+        ph[e] = (__bf16)pe;
+        plo[e] = (__bf16)(pe - (float)ph[e]);
+      }
+      __builtin_memcpy(&pf[k], ph, sizeof(bf16x8));
+      __builtin_memcpy(&pl[k], plo, sizeof(bf16x8));
     }
     if (__ballot(mref != mold) != 0ull) {  // wave-uniform: rare after the first tile
       const float alpha = fast_exp2(mold - muse);
@@ -220,8 +238,6 @@ __device__ __forceinline__ void tile_softmax(float (&x)[RB][8], float scale_log2
     }
     st.l[k] += sum;
     st.m[k] = mref;
-    __builtin_memcpy(&pf[k], ph, sizeof(bf16x8));
-    __builtin_memcpy(&pl[k], plo, sizeof(bf16x8));
   }
 }
 

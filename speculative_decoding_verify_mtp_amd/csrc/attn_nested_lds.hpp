@@ -136,7 +136,7 @@ __device__ __forceinline__ void nest_scores_u(const bf16x8 (&qs)[RB][4], const b
   }
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
-    const float mx = mul_rn(rows4_max(max8(x[k])), sl2r[k]);
+    const float mx = mul_rn(rows4_maximum(max8(x[k])), sl2r[k]);
     const float mold = st.m[k];
     const float mref = mx > mold + kRescaleSlack ? mx : mold;
     const float muse = mref == neg_inf() ? 0.f : mref;

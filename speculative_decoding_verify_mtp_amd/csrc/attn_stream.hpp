@@ -361,7 +361,7 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
             if (((vrow[k] >> (j0 + pv_key(qd, e))) & 1ull) == 0ull) x[k][e] = neg_inf();
       }
       bf16x8 pf[RB], pl[RB];
-      tile_softmax<D, RB>(x, p.scale_log2, st, pf, pl, [](int, int) { return true; });
+      tile_softmax<D, RB, false>(x, p.scale_log2, st, pf, pl, [](int, int) { return true; });
       tile_pv<D, RB>(pf, pl, vv, st);
     }
     wait_vmem_barrier<0>();  // every wave is done with the ring before the next run fills it
