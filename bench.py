@@ -36,10 +36,14 @@ HBM_PEAK_GBS = 8000.0
 # The headline: the 64-sequence ragged batch (4.9 GB of paged KV), the largest
 # workload and the one whose step is bound by HBM bandwidth.
 DEFAULT_WORKLOAD = "ragged_batch"
-# The first launches of a process over a multi-GB pool run slower (page-table
-# and TLB warm-up: about 20 launches at 1.1-1.3 ms before settling near
-# 0.95 ms on the ragged batch), so at least this many untimed steps run first.
+# The first launches of a process over a multi-GB pool run slower, and not
+# only the first few: on the ragged batch (kernel trace) launches 0-20 take
+# 0.94-1.22 ms, 20-40 about 0.90-0.94 ms, and the partial kernel settles near
+# 0.87-0.89 ms only after about 150 ms of work (clocks and page-table / TLB
+# warm-up).  So at least MIN_WARMUP_STEPS untimed steps run first, and the
+# untimed steps continue until MIN_WARMUP_SECONDS of them have run.
 MIN_WARMUP_STEPS = 24
+MIN_WARMUP_SECONDS = 0.5
 # Bytes that stay resident between two reads of one KV replica only if they
 # fit the 256 MB Infinity Cache; a step whose replicas exceed it reads cold.
 MALL_BYTES = 256 << 20
@@ -642,9 +646,15 @@ def main() -> int:
 
     warm_steps = max(args.warmup, MIN_WARMUP_STEPS)
     wreps = math.ceil(warm_steps / NG)
+    tw = time.perf_counter()
     for _ in range(wreps):
         g_step.replay()
     torch.cuda.synchronize()
+    while time.perf_counter() - tw < MIN_WARMUP_SECONDS:  # until the clocks have settled
+        for _ in range(4):
+            g_step.replay()
+        wreps += 4
+        torch.cuda.synchronize()
     # one event after each replay: per-replay step times give the spread
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
     t0 = time.perf_counter()
@@ -663,7 +673,7 @@ def main() -> int:
     # dominant kernel: HIP events around replays of the partial-only graph
     preps = max(1, math.ceil(args.steps / NG))
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(wreps):
+    for _ in range(math.ceil(warm_steps / NG)):  # the device is warm by now
         g_part.replay()
     p0.record()
     for _ in range(preps):
