@@ -332,8 +332,14 @@ def bench_nested_attn(wl: I.Workload, inp: dict, args) -> int:
                     run(r, phase)
         torch.cuda.synchronize()
         reps = max(1, math.ceil(args.steps / R))
+        tw = time.perf_counter()
         for _ in range(max(1, math.ceil(args.warmup / R))):
             g.replay()
+        torch.cuda.synchronize()
+        while time.perf_counter() - tw < MIN_WARMUP_SECONDS:  # until the clocks have settled
+            for _ in range(4):
+                g.replay()
+            torch.cuda.synchronize()
         a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
