@@ -10,7 +10,9 @@ runs the whole step (mtp_verify_step: attention, then acceptance and commit
 in the finish launch) and compares every output with the oracle: attention
 within the stated tolerance, acceptance, context lengths and the committed
 cache bytes bit-exact.  A second set draws shapes for the nested KV4 / KV8
-cache (bf16, D = 128) and its KV8, KV4 and Recent-N reads.
+cache (bf16, D = 128) and its KV8, KV4 and Recent-N reads, a third for the
+dynamic token tree builder (draft ids, parents, depths and node counts
+bit-exact).
 """
 from __future__ import annotations
 
@@ -120,3 +122,32 @@ def test_random_shape_nested_attention_matches_oracle(wl, recent):
         inp["k_new"].double().cpu().numpy(), inp["v_new"].double().cpu().numpy(),
         ints(inp["mask_kind"]), ints(inp["mask_ids"]), inp["scale"], inp["seg_lookback"], recent)
     assert_attn_close(out, lse, ref_out, ref_lse, *tol_for(wl), what=f"{wl.name} recent={recent}")
+
+
+def random_trees(n: int, seed: int) -> list[tuple]:
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 7))
+        K = int(rng.choice([1, 2, 5, 8, 13, 32, 64]))
+        V = int(rng.choice([1, 2, 9, 100, 1000, 4096]))
+        W = int(rng.choice([1, 2, 7, 16, 33, 64]))
+        n_mask = int(rng.integers(0, min(W, 9)))
+        thr = float(rng.choice([0.0, 0.0, 1e-4, 1e-2]))
+        peak = float(rng.choice([0.5, 2.0, 8.0]))
+        out.append((B, K, V, W, n_mask, thr, peak))
+    return out
+
+
+TREES = random_trees(24, 6077)
+
+
+@pytest.mark.parametrize("case", TREES, ids=[str(c) for c in TREES])
+def test_random_shape_tree_matches_oracle(case):
+    B, K, V, W, n_mask, thr, peak = case
+    inp = I.make_tree_inputs(B, K, V, 57 + K + V + W, peak=peak, device="cuda")
+    got = lib.build_tree(inp["probs"], inp["root"], W, n_mask, thr)
+    torch.cuda.synchronize()
+    ref = O.dynamic_tree(inp["host"]["probs"], inp["host"]["root"], W, n_mask, thr)
+    for g, r, name in zip(got, ref, ("draft", "parents", "depth", "n_nodes")):
+        assert np.array_equal(ints(g), r), f"{case} {name}: {ints(g)} != {r}"
