@@ -112,10 +112,12 @@ int32_t mtp_abi_version(void);
 /* Static text for a status code (never NULL). */
 const char* mtp_status_string(int32_t status);
 
-/* Bytes of device workspace mtp_verify_attn needs for `shape` (split-K
- * partials: per sequence, split, KV head and block-row x group-member row,
- * D accumulators plus running max and sum, fp32).  Depends on B, W, Hq, Hkv,
- * D, dtype, max_ctx_len and split_tokens only. */
+/* Bytes of device workspace mtp_verify_attn and mtp_verify_step need for
+ * `shape` (split-K partials: per sequence, split, KV head and block-row x
+ * group-member row, D accumulators plus running max and sum, fp32; then
+ * B * W int32 row targets, which mtp_verify_step may hand from its partial
+ * launch to its acceptance).  Depends on B, W, Hq, Hkv, D, dtype,
+ * max_ctx_len and split_tokens only. */
 mtp_status mtp_verify_attn_workspace_size(const mtp_shape* shape, size_t* bytes);
 
 /* Verify attention (the step's attention over committed + in-block keys).

@@ -21,6 +21,7 @@ namespace mtpv {
 
 struct AcceptParams {
   const float* logits;  // [B, W, V]
+  const int32_t* tgt = nullptr;  // [B, W] row argmaxes already found (nullptr: from logits)
   const int32_t* draft_ids;
   const uint8_t* mask_kind;
   const int32_t* mask_ids;
@@ -185,6 +186,13 @@ __device__ __forceinline__ void block_argmax(const AcceptParams& p, int b, int* 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
+  if (p.tgt != nullptr) {  // found by the launch before (the step's target prologue)
+    int t = 0;
+    if (wv == 0 && lane < p.W) t = p.tgt[(size_t)b * p.W + lane];
+    mid();
+    if (wv == 0 && lane < p.W) s_tgt[lane] = t;
+    return;
+  }
   const bool vec = rows_vec(p.logits, p.V);
   const float* base = p.logits + (size_t)b * p.W * p.V;
   if (vec && p.V <= kRegV) {

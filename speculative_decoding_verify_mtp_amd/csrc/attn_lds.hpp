@@ -25,6 +25,7 @@
 // and serialise the pipeline.
 #pragma once
 
+#include "accept_commit.hpp"
 #include "attn_mfma.hpp"
 #include "common.hpp"
 
@@ -173,7 +174,18 @@ void attn_partial_lds(AttnParams p) {
   // trip before the first stage is issued
   const int mkind = p.mask_kind[b];
   const int mid = lane_mask_id(p, b, lane);
-  const int L = p.ctx_lens[b];
+  // the step's target prologue: wave 0 of workgroup j < B * W finds the
+  // argmax of logits row j, its loads in the same round trip as the set-up
+  // (the host enables it for V <= kRegV, V % 4 == 0, 16-byte aligned rows;
+  // the reduction is the acceptance's own, so the targets are the same)
+  const int L = p.ctx_lens[b];  // requested before the prologue waits for its row
+  const int flat = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  if (p.logits != nullptr && flat < p.B * p.W && wv == 0) {
+    RegRow rr;
+    load_reg_row(p.logits + (size_t)flat * p.V, p.V, rr);
+    const int t = reg_row_argmax(rr, p.V);
+    if (lane == 0) p.tgt[flat] = t;
+  }
   if (L < 0 || L > p.max_ctx) return;
   const int ns = num_splits(p, L);
   if (it.split >= ns) return;

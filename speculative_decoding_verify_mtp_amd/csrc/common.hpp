@@ -182,6 +182,13 @@ struct AttnParams {
   int max_splits;  // splits of max_ctx
   int max_pages, num_pages, max_ctx, lookback;
   float scale_log2;  // softmax scale * log2(e)
+  // The step's target prologue (per-split LDS kernel; logits == nullptr:
+  // off): workgroup j < B * W of the launch also writes tgt[j], the argmax
+  // of logits row j ([B, W, V] fp32), so that the acceptance after the
+  // launch reads W targets instead of W rows of V logits.
+  const float* logits = nullptr;
+  int32_t* tgt = nullptr;
+  int V = 0;
 };
 
 // Work item of the split-K kernels: (row block, KV head, split) of sequence

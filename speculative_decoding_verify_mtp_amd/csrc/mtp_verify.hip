@@ -57,7 +57,7 @@ mtp_status mtp_verify_attn_workspace_size(const mtp_shape* shape, size_t* bytes)
   if (st != MTP_OK) return st;
   if (bytes == nullptr) return MTP_ERR_NULL;
   const Plan pl = make_plan(*shape);
-  *bytes = pl.seg_offset + pl.seg_bytes;
+  *bytes = pl.ws_bytes;
   return MTP_OK;
 }
 
@@ -66,7 +66,7 @@ mtp_status mtp_verify_attn_nested_workspace_size(const mtp_shape* shape, size_t*
   if (st != MTP_OK) return st;
   if (bytes == nullptr) return MTP_ERR_NULL;
   const Plan pl = make_plan(*shape, true);
-  *bytes = pl.seg_offset + pl.seg_bytes;
+  *bytes = pl.ws_bytes;
   return MTP_OK;
 }
 
@@ -97,7 +97,7 @@ mtp_status build_attn(const mtp_shape* shape, const void* q, const void* k_cache
     return MTP_ERR_NULL;
   a.pl = make_plan(s, nested);
   const Plan& pl = a.pl;
-  if (workspace_bytes < pl.seg_offset + pl.seg_bytes || ((uintptr_t)workspace & 15) != 0)
+  if (workspace_bytes < pl.ws_bytes || ((uintptr_t)workspace & 15) != 0)
     return MTP_ERR_WORKSPACE;
   AttnParams& p = a.p;
   p.q = q;
@@ -219,10 +219,13 @@ unsigned combine_blocks(const AttnParams& p, const Plan& pl, bool finish, int wa
 
 // Compute units the combine workgroups of the step's finish launch may take:
 // those the B acceptance workgroups leave free; with the per-split layout
-// (one row per wave) at most kFinishSplitCUs of them.  The acceptance
-// workgroups run a chain of dependent loads beside the combine, and fewer
-// combine workgroups in flight leave their loads less to queue behind
-// (llama3_8b_tree step 29.9 -> 29.3 us, the other workloads unchanged).
+// (one row per wave) at most kFinishSplitCUs of them when the acceptance
+// reduces the logits rows itself: its chain of dependent loads runs beside
+// the combine, and fewer combine workgroups in flight leave its loads less
+// to queue behind (llama3_8b_tree step 29.9 -> 29.3 us).  When the partial
+// launch found the targets (step_target_prologue) the acceptance reads W
+// words instead, and the combine takes every free CU (llama3_8b_tree step
+// 24.7 -> 24.0 us).
 constexpr long kFinishSplitCUs = 128;
 long finish_combine_cus(const AttnParams& p, const Plan& pl) {
   // More sequences than half the compute units: their acceptance workgroups
@@ -230,7 +233,8 @@ long finish_combine_cus(const AttnParams& p, const Plan& pl) {
   // (looping) combine a handful of workgroups for the whole batch; it keeps
   // one workgroup per compute unit instead, dispatched behind them.
   const long free_cus = p.B <= kCUs / 2 ? (long)kCUs - p.B : (long)kCUs;
-  return grouped_combine(p, pl, true) ? free_cus : std::min(kFinishSplitCUs, free_cus);
+  if (grouped_combine(p, pl, true) || p.logits != nullptr) return free_cus;
+  return std::min(kFinishSplitCUs, free_cus);
 }
 
 // Combine waves per workgroup of the step's finish launch.  Its workgroups
@@ -434,6 +438,14 @@ mtp_status mtp_verify_step(const mtp_shape* shape, const void* q, void* k_cache,
                    ctx_lens_out, skip_root, k_cache, v_cache, true, cp);
   if (st != MTP_OK || shape->B == 0) return st;
   hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (ctx_lens_out != ctx_lens_in && step_target_prologue(a.pl, *shape, logits, V)) {
+    // the partial launch finds the row targets; the acceptance reads them
+    int32_t* tgt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + a.pl.tgt_offset);
+    a.p.logits = logits;
+    a.p.tgt = tgt;
+    a.p.V = V;
+    ap.tgt = tgt;
+  }
   launch_partial(a, shape->D, shape->dtype, shape->B, strm);
   if (ctx_lens_out == ctx_lens_in) {  // the combine reads what the commit writes: serialise
     launch_combine(a, shape->D, strm);
@@ -503,7 +515,7 @@ mtp_status mtp_verify_step_noalloc(const mtp_shape* shape, const void* q, void* 
   const mtp_status st = check_shape(shape);
   if (st != MTP_OK) return st;
   const Plan pl = make_plan(*shape);
-  if (pl.seg_offset + pl.seg_bytes > kScratchBytes) return MTP_ERR_SCRATCH;
+  if (pl.ws_bytes > kScratchBytes) return MTP_ERR_SCRATCH;
   void* ws = nullptr;
   if (shape->B > 0) {
     const mtp_status ss = scratch_of_current_device(&ws);

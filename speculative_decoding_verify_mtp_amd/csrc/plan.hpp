@@ -72,6 +72,8 @@ struct Plan {
   bool piece_rows; // stream layout with many pieces per segment: the combine takes a row per wave
   int nts, nseg, rows_block;
   size_t acc_bytes, ml_offset, ml_bytes, seg_offset, seg_bytes;
+  size_t tgt_offset, tgt_bytes;  // the step's row targets (B * W int32)
+  size_t ws_bytes;               // the whole workspace
 };
 
 mtp_status check_shape(const mtp_shape* s) {
@@ -261,7 +263,20 @@ Plan make_plan(const mtp_shape& s, bool nested = false) {
   pl.ml_bytes = rows * 2 * sizeof(float);
   pl.seg_offset = (pl.ml_offset + pl.ml_bytes + 255) & ~(size_t)255;
   pl.seg_bytes = stream_layout(pl.kernel) ? (size_t)s.B * pl.nseg * 2 * sizeof(int) : 0;
+  pl.tgt_offset = (pl.seg_offset + pl.seg_bytes + 255) & ~(size_t)255;
+  pl.tgt_bytes = (size_t)s.B * s.W * sizeof(int32_t);
+  pl.ws_bytes = pl.tgt_offset + pl.tgt_bytes;
   return pl;
+}
+
+// The step's target prologue (AttnParams::logits): on the per-split LDS
+// kernel, whose first B * W workgroups find one logits row's argmax each,
+// for rows the acceptance would reduce from registers (V <= kRegV, V % 4 ==
+// 0, 16-byte aligned).
+bool step_target_prologue(const Plan& pl, const mtp_shape& s, const float* logits, int V) {
+  const long wgs = (long)pl.max_splits * s.Hkv * pl.nRB * s.B;
+  return pl.kernel == kMfmaLds && logits != nullptr && V >= 1 && V <= kRegV && V % 4 == 0 &&
+         ((uintptr_t)logits & 15) == 0 && (long)s.B * s.W <= wgs;
 }
 
 }  // namespace

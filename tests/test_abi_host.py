@@ -195,7 +195,8 @@ def expected_workspace(B, W, Hq, Hkv, D, dtype, max_ctx, split=0):
         seg = B * nseg * 8
     acc = rows * D * 4
     a256 = lambda x: ((x + 255) // 256) * 256
-    return a256(a256(acc) + rows * 8) + seg
+    # then the step's row targets, B * W int32
+    return a256(a256(a256(acc) + rows * 8) + seg) + B * W * 4
 
 
 @pytest.mark.parametrize("kw", [

@@ -358,6 +358,46 @@ def test_accept_argmax_ties_take_the_smallest_id():
     assert list(ints(got[0])) == [3, 1, 3]
 
 
+STEP_TARGETS = [
+    # the partial launch finds the row targets (V <= 1024, V % 4 == 0) ...
+    W_("targets_v1000", B=2, Hq=32, Hkv=8, W=32, ctx_lo=300, ctx_hi=900, masks="tree"),
+    W_("targets_v4", B=1, Hq=20, Hkv=5, W=8, ctx_lo=500, ctx_hi=500, vocab=4),
+    # ... or the acceptance reduces the rows itself
+    W_("targets_v1001", B=1, Hq=20, Hkv=5, W=8, ctx_lo=500, ctx_hi=500, vocab=1001),
+    W_("targets_v3000", B=2, Hq=16, Hkv=4, W=16, ctx_lo=200, ctx_hi=600, masks="mixed",
+       vocab=3000),
+]
+
+
+@pytest.mark.parametrize("wl", STEP_TARGETS, ids=[w.name for w in STEP_TARGETS])
+@pytest.mark.parametrize("ties", [False, True])
+def test_step_targets_match_oracle(wl, ties):
+    """Acceptance through the whole step, on both routes of the row targets;
+    with ties, every logits row repeats its maximum at later ids, so the
+    smallest id must win on either route."""
+    inp = gpu_inputs(wl, 25)
+    if ties:
+        lg = inp["logits"]
+        mx = lg.max(dim=2, keepdim=True).values
+        am = lg.argmax(dim=2, keepdim=True)
+        ids = torch.arange(lg.shape[2], device=lg.device).view(1, 1, -1)
+        lg[:] = torch.where(((ids - am) % 3 == 0) & (ids > am), mx.expand_as(lg), lg)
+    n_ref, path_ref, bonus_ref = oracle_accept(inp)
+    kc_ref, vc_ref, ctx_ref = O.kv_commit(raw(inp["k_cache"]), raw(inp["v_cache"]),
+                                          raw(inp["k_new"]), raw(inp["v_new"]), n_ref, path_ref,
+                                          ints(inp["block_table"]), ints(inp["ctx_lens"]))
+    out, lse, n, path, bonus, ctx_out = lib.verify_step(
+        inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["ctx_lens"],
+        inp["k_new"], inp["v_new"], inp["mask_kind"], inp["mask_ids"], inp["logits"],
+        inp["draft_ids"], ctx_lens_out=torch.full_like(inp["ctx_lens"], -3),
+        max_ctx_len=int(inp["host"]["ctx_lens"].max()), scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert_accept_equal((n, path, bonus), (n_ref, path_ref, bonus_ref))
+    assert np.array_equal(ints(ctx_out), ctx_ref)
+    assert np.array_equal(raw(inp["k_cache"]), kc_ref)
+    assert np.array_equal(raw(inp["v_cache"]), vc_ref)
+
+
 def tie_block(tgt: np.ndarray, V: int):
     """Four tree blocks of width 8 whose siblings share drafted ids, so that
     several equally deep nodes are accepted.  Returns (parents, drafts,
