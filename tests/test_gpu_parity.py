@@ -715,6 +715,13 @@ STEP = [
     W_("step_stream_b1", B=1, Hq=32, Hkv=8, W=16, ctx_lo=9000, ctx_hi=9000, masks="tree"),
     W_("step_grouped_b4", B=4, Hq=64, Hkv=8, W=16, ctx_lo=50, ctx_hi=600, masks="mixed"),
     W_("step_chain_b1", B=1, Hq=20, Hkv=5, W=8, ctx_lo=600, ctx_hi=600),
+    # one sequence of 4000 tokens on the per-split kernel with key slices
+    # (32 splits of 128 tokens); 38 and 47 splits of 32 tokens on the D = 64
+    # and fp32 kernels (the finish launch's combine takes a second batch)
+    W_("step_chain_b1_long", B=1, Hq=20, Hkv=5, W=8, ctx_lo=4000, ctx_hi=4000),
+    W_("step_segment_d64_38_splits", B=1, Hq=16, Hkv=16, D=64, W=16, ctx_lo=1200, ctx_hi=1200,
+       masks="segment", seg_lookback=1),
+    W_("step_fp32_47_splits", B=1, Hq=4, Hkv=4, W=4, dtype="f32", ctx_lo=1500, ctx_hi=1500),
     W_("step_segment_d64", B=3, Hq=16, Hkv=16, D=64, W=16, ctx_lo=30, ctx_hi=300,
        masks="segment", seg_lookback=1),
     W_("step_fp32", B=2, Hq=4, Hkv=4, D=64, W=4, dtype="f32", ctx_lo=100, ctx_hi=256),
