@@ -416,8 +416,7 @@ void attn_partial_lds(AttnParams p) {
       const float l = rows4_sum(st.l[0]);
       const int rho = row_tile0 * 16 + c;
       if (qd == 0 && rho < p.R) {
-        p.part_ml[2 * (item_row + rho)] = st.m[0];
-        p.part_ml[2 * (item_row + rho) + 1] = l;
+        store_partial_ml(p.part_ml + 2 * item_row, 2 * rho, st.m[0], l);
       }
       // float4 j of lane (c, qd) holds row c, d = qd * D / 4 + 4 j .. + 4
       float* rowp = sbuf + (size_t)(tg * 16 + c) * kPitch + qd * (D / 4);
@@ -436,8 +435,8 @@ void attn_partial_lds(AttnParams p) {
       const int row = f / (D / 4);
       const int col = f - row * (D / 4);
       if (row0 + row < p.R)
-        *reinterpret_cast<float4*>(p.part_acc + (item_row + row0 + row) * D + col * 4) =
-            *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4);
+        store_partial4(p.part_acc + item_row * D, (row0 + row) * D + col * 4,
+                       *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4));
     }
     return;
   }
@@ -464,8 +463,7 @@ void attn_partial_lds(AttnParams p) {
     const float l = rows4_sum(st.l[k]);
     const int rho = (row_tile0 + k) * 16 + c;
     if (qd == 0 && rho < p.R) {
-      p.part_ml[2 * (item_row + rho)] = st.m[k];
-      p.part_ml[2 * (item_row + rho) + 1] = l;
+      store_partial_ml(p.part_ml + 2 * item_row, 2 * rho, st.m[k], l);
     }
     float* rowp = sbuf + (size_t)((tg * RB + k) * 16 + c) * kPitch + qd * (D / 4);
 #pragma unroll
@@ -483,8 +481,8 @@ void attn_partial_lds(AttnParams p) {
     const int row = f / (D / 4);
     const int col = f - row * (D / 4);
     if (row0 + row < p.R)
-      *reinterpret_cast<float4*>(p.part_acc + (item_row + row0 + row) * D + col * 4) =
-          *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4);
+      store_partial4(p.part_acc + item_row * D, (row0 + row) * D + col * 4,
+                     *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4));
   }
 }
 

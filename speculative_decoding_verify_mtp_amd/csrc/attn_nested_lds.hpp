@@ -495,10 +495,7 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
     for (int k = 0; k < RB; ++k) {
       const float l = rows4_sum(st.l[k]);
       const int rho = (row_tile0 + k) * 16 + c;
-      if (qd == 0 && rho < p.R) {
-        p.part_ml[2 * (item_row + rho)] = st.m[k];
-        p.part_ml[2 * (item_row + rho) + 1] = l;
-      }
+      if (qd == 0 && rho < p.R) store_partial_ml(p.part_ml + 2 * item_row, 2 * rho, st.m[k], l);
       float* rowp = sbuf + (size_t)((wv * RB + k) * 16 + c) * kPitch + qd * (D / 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -515,8 +512,8 @@ void attn_partial_nested_lds(AttnParams p, NestedAttn na) {
       const int row = f / (D / 4);
       const int col = f - row * (D / 4);
       if (row0 + row < p.R)
-        *reinterpret_cast<float4*>(p.part_acc + (item_row + row0 + row) * D + col * 4) =
-            *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4);
+        store_partial4(p.part_acc + item_row * D, (row0 + row) * D + col * 4,
+                       *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4));
     }
   } else {
 #pragma unroll

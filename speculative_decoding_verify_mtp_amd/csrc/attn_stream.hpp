@@ -388,11 +388,8 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
         for (int k = 0; k < RB; ++k) {
           const float l = rows4_sum(st.l[k]);
           const int rl = (wv * RB + k) * 16 + c;  // row within the block
-          if (qd == 0 && rb * sp.rows_block + rl < p.R) {
-            const size_t pidx = piece * sp.rows_block + rl;
-            p.part_ml[2 * pidx] = st.m[k];
-            p.part_ml[2 * pidx + 1] = l;
-          }
+          if (qd == 0 && rb * sp.rows_block + rl < p.R)
+            store_partial_ml(p.part_ml + 2 * piece * sp.rows_block, 2 * rl, st.m[k], l);
           float* rowp = sbuf + (size_t)rl * kPitch + qd * (D / 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -407,8 +404,8 @@ void attn_partial_stream(AttnParams p, StreamParams sp) {
           const int row = f / (D / 4);
           const int col = f - row * (D / 4);
           if (rb * sp.rows_block + row < p.R)
-            *reinterpret_cast<float4*>(p.part_acc + (piece * sp.rows_block + row) * D + col * 4) =
-                *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4);
+            store_partial4(p.part_acc + piece * sp.rows_block * D, row * D + col * 4,
+                           *reinterpret_cast<const float4*>(sbuf + (size_t)row * kPitch + col * 4));
         }
         // the next run refills the ring: every wave is done reading the rows
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");

@@ -38,6 +38,44 @@ __host__ __device__ inline bool grouped_split_combine(int max_splits, long rows)
   return max_splits <= kGroupedMaxSplits && rows >= kGroupedMinRows;
 }
 
+// Stores of partial rows (split partials, stream pieces) that a kernel
+// writes as whole rows (1 KB per store instruction) and the next launch
+// reads on any XCD.  With the sc1 cache policy the L2 writes them through as
+// they are stored; plain stores leave them dirty in the writer's L2, to be
+// written back at the end of the launch before the next one may start (the
+// per-split kernel on one sequence: bitnet2b_chain step 14.2 -> 13.7 us,
+// llama3_8b_tree 24.6 -> 23.2 us, its nested KV8 form 27.9 -> 26.5 us; the
+// stream kernel's ragged batch step 903 -> 899 us).  Stores of 16-byte
+// pieces of rows straight from registers stay plain, merged into whole lines
+// in the L2 (written through, the D = 64 direct kernel's lca_segments
+// partial took 53.0 -> 55.6 us), and so do the nested stream kernel's
+// (ragged batch KV8 900 -> 913 us written through).
+// `base` is wave-uniform (it becomes a buffer resource in scalar
+// registers); `i` counts floats from it, below 2^29.
+constexpr int kCpolSc1 = 16;  // cache-policy operand of the buffer builtins: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base) {
+  // the base from the first active lane (the same in every lane), so that
+  // the resource is built in scalar registers without a loop over lanes
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  float* u = reinterpret_cast<float*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+  // num_records: 2^31 - 1 bytes; word 3: 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, 0x7fffffff, 0x00020000);
+}
+// base[i] = m, base[i + 1] = l
+__device__ __forceinline__ void store_partial_ml(float* base, int i, float m, float l) {
+  const __amdgpu_buffer_rsrc_t r = partial_rsrc(base);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), r, i * 4, 0, kCpolSc1);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), r, i * 4 + 4, 0, kCpolSc1);
+}
+// base[i .. i + 3] = v (16-byte aligned)
+__device__ __forceinline__ void store_partial4(float* base, int i, float4 v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(u, partial_rsrc(base), i * 4, 0, kCpolSc1);
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
 
