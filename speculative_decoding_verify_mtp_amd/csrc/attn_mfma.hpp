@@ -465,34 +465,38 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams p) {
     }
   }
 
-  // Store the partial (m, l, unnormalised acc) of every real row.
+  // Store the partial (m, l, unnormalised acc) of every real row: each wave
+  // lays a 16-row tile out row-major in its own LDS region, then stores
+  // whole rows written through the L2.
+  constexpr int kPitch = D + 4;
+  __shared__ float stage_rows[4][16 * kPitch];
+  float* sw = stage_rows[threadIdx.x >> 6];
+  const size_t item_row = (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R;
 #pragma unroll
   for (int k = 0; k < RB; ++k) {
     float l = st.l[k];
     l = rows4_sum(l);
-    const int rho = (it.rb * RB + k) * 16 + c;
-    if (rho < p.R) {
-      const size_t pidx =
-          (((size_t)b * p.max_splits + it.split) * p.Hkv + it.kvh) * (size_t)p.R + rho;
-      if (qd == 0) {
-        p.part_ml[2 * pidx] = st.m[k];
-        p.part_ml[2 * pidx + 1] = l;
-      }
-      float* dst = p.part_acc + pidx * D + qd * (D / 4);
-      // lane holds d = qd*D/4 + e*(D/16) + t in acc[k][t][e]
+    const int rho0 = (it.rb * RB + k) * 16;
+    const int rho = rho0 + c;
+    if (qd == 0 && rho < p.R) store_partial_ml(p.part_ml + 2 * item_row, 2 * rho, st.m[k], l);
+    float* rowp = sw + c * kPitch + qd * (D / 4);
+    // lane holds d = qd*D/4 + e*(D/16) + t in acc[k][t][e]
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int t = 0; t < NT; t += 4) {
-          float4 v;
-          v.x = st.acc[k][t][e];
-          v.y = st.acc[k][t + 1][e];
-          v.z = st.acc[k][t + 2][e];
-          v.w = st.acc[k][t + 3][e];
-          *reinterpret_cast<float4*>(dst + e * (D / 16) + t) = v;
-        }
-      }
+      for (int t = 0; t < NT; t += 4)
+        *reinterpret_cast<float4*>(rowp + e * (D / 16) + t) =
+            make_float4(st.acc[k][t][e], st.acc[k][t + 1][e], st.acc[k][t + 2][e], st.acc[k][t + 3][e]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int f = lane; f < 16 * (D / 4); f += kWave) {
+      const int row = f / (D / 4);
+      const int col = f - row * (D / 4);
+      if (rho0 + row < p.R)
+        store_partial4(p.part_acc + item_row * D, (rho0 + row) * D + col * 4,
+                       *reinterpret_cast<const float4*>(sw + row * kPitch + col * 4));
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 

@@ -45,11 +45,12 @@ __host__ __device__ inline bool grouped_split_combine(int max_splits, long rows)
 // written back at the end of the launch before the next one may start (the
 // per-split kernel on one sequence: bitnet2b_chain step 14.2 -> 13.7 us,
 // llama3_8b_tree 24.6 -> 23.2 us, its nested KV8 form 27.9 -> 26.5 us; the
-// stream kernel's ragged batch step 903 -> 899 us).  Stores of 16-byte
-// pieces of rows straight from registers stay plain, merged into whole lines
-// in the L2 (written through, the D = 64 direct kernel's lca_segments
-// partial took 53.0 -> 55.6 us), and so do the nested stream kernel's
-// (ragged batch KV8 900 -> 913 us written through).
+// stream kernel's ragged batch step 903 -> 899 us; the D = 64 direct
+// kernel, staging its rows through LDS for this, lca_segments 61.05 ->
+// 60.86 us).  Stores of 16-byte pieces of rows straight from registers stay
+// plain, merged into whole lines in the L2 (written through, the direct
+// kernel's lca_segments partial took 53.0 -> 55.6 us), and so do the nested
+// stream kernel's (ragged batch KV8 900 -> 913 us written through).
 // `base` is wave-uniform (it becomes a buffer resource in scalar
 // registers); `i` counts floats from it, below 2^29.
 constexpr int kCpolSc1 = 16;  // cache-policy operand of the buffer builtins: sc1
